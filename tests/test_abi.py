@@ -1,0 +1,118 @@
+"""The C-ABI library loads on the CPU, exports every entry point the header
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import speculative_decoding_verification_accept_amd as sv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b(spec_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(sv.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return sv.load_library()
+
+
+def test_header_declares_the_boundary():
+    fns = _declared_functions()
+    assert fns == sorted(["spec_accept", "spec_accept_workspace_bytes", "spec_verify_linear",
+                          "spec_verify_linear_workspace_bytes", "spec_status_string",
+                          "spec_abi_version"]), fns
+    assert sorted(n for n, _, _ in sv.ABI) == fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.spec_abi_version() == 1
+    assert sv.status_string(0) == "ok"
+    assert "invalid" in sv.status_string(-1)
+
+
+def test_workspace_sizes(lib):
+    assert lib.spec_accept_workspace_bytes(-1, 4, 10) == 0
+    assert lib.spec_accept_workspace_bytes(8, 256, 10) == 0
+    n = lib.spec_accept_workspace_bytes(64, 7, 128256)
+    # 16 chunks of 8192 entries: 16-byte partials per (row, position, chunk),
+    # an fp64 residual mass per (row, chunk) and a counter per row
+    assert n >= 64 * 8 * 16 * 16 + 64 * 16 * 8 + 64 * 4
+    assert n % 256 == 0
+    assert lib.spec_verify_linear_workspace_bytes(0, 8, 8) == 0
+
+
+FAKE = ctypes.c_void_p(0x100000)     # never dereferenced: validation fails first
+FAKE_ODD = ctypes.c_void_p(0x100004)
+
+
+def _accept(lib, **kw):
+    a = dict(z=FAKE, dt=0, q=FAKE, x=FAKE, L=None, B=2, K=3, V=100, rb=0, T=1.0,
+             seed=1, off=0, ot=FAKE, oa=FAKE, op=None, os=None, ws=FAKE, wsb=1 << 30, st=None)
+    a.update(kw)
+    return lib.spec_accept(a["z"], a["dt"], a["q"], a["x"], a["L"], a["B"], a["K"], a["V"],
+                           a["rb"], a["T"], a["seed"], a["off"], a["ot"], a["oa"], a["op"],
+                           a["os"], a["ws"], a["wsb"], a["st"])
+
+
+def test_accept_argument_validation(lib):
+    E = sv.SPEC_ERR_INVALID_ARG
+    assert _accept(lib, B=-1) == E
+    assert _accept(lib, K=-1) == E
+    assert _accept(lib, K=256) == E
+    assert _accept(lib, V=0) == E
+    assert _accept(lib, rb=-1) == E
+    assert _accept(lib, rb=2**32 - 1) == E          # row_base + B overflows the 32-bit row word
+    assert _accept(lib, dt=7) == E
+    assert _accept(lib, T=-0.5) == E
+    assert _accept(lib, T=float("nan")) == E
+    assert _accept(lib, T=float("inf")) == E
+    assert _accept(lib, z=None) == E
+    assert _accept(lib, ot=None) == E
+    assert _accept(lib, oa=None) == E
+    assert _accept(lib, x=None) == E
+    assert _accept(lib, q=None) == E                 # stochastic mode needs q
+    assert _accept(lib, B=1 << 22, K=7, V=128256) == E  # grid limit
+    assert _accept(lib, ws=None) == sv.SPEC_ERR_WORKSPACE
+    assert _accept(lib, wsb=16) == sv.SPEC_ERR_WORKSPACE
+    assert _accept(lib, ws=FAKE_ODD) == sv.SPEC_ERR_WORKSPACE
+    assert _accept(lib, B=0) == sv.SPEC_OK           # nothing to do, nothing launched
+
+
+def test_linear_argument_validation(lib):
+    E = sv.SPEC_ERR_INVALID_ARG
+    f = lib.spec_verify_linear
+    assert f(FAKE, FAKE, FAKE, 0, -1, 64, 64, None, 0, None) == E
+    assert f(FAKE, FAKE, FAKE, 0, 4, 0, 64, None, 0, None) == E
+    assert f(FAKE, FAKE, FAKE, 0, 4, 60, 64, None, 0, None) == E    # N % 8
+    assert f(FAKE, FAKE, FAKE, 0, 4, 64, 60, None, 0, None) == E    # K % 8
+    assert f(FAKE, FAKE, FAKE, 5, 4, 64, 64, None, 0, None) == E    # dtype
+    assert f(None, FAKE, FAKE, 0, 4, 64, 64, None, 0, None) == E
+    assert f(FAKE_ODD, FAKE, FAKE, 0, 4, 64, 64, None, 0, None) == E
+    assert f(FAKE, FAKE, FAKE, 0, 0, 64, 64, None, 0, None) == sv.SPEC_OK
+    need = lib.spec_verify_linear_workspace_bytes(4, 14336, 4096)
+    assert need > 0
+    assert f(FAKE, FAKE, FAKE, 0, 4, 14336, 4096, None, 0, None) == sv.SPEC_ERR_WORKSPACE
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    z = torch.zeros(1, 2, 8)
+    with pytest.raises(ValueError):
+        sv.accept(z, torch.zeros(1, 1, 8), torch.zeros(1, 1, dtype=torch.int32),
+                  temperature=1.0, seed=0)
+    with pytest.raises(ValueError):
+        sv.verify_linear(torch.zeros(2, 8, dtype=torch.bfloat16),
+                         torch.zeros(8, 8, dtype=torch.bfloat16))
