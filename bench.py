@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""Benchmark of the speculative-decoding verification step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+the verify linear layer on the lm-head (hidden [B(K+1), 4096] bf16 x W
+[4096, 151936] bf16 -> fp32 logits) followed by the accept/reject pass over
+those logits (B = 32 rows, K = 5 drafts, T = 0.6).  The headline value is
+verified positions per second (B(K+1) per step).  The draft side (draft
+probabilities from noisy target logits, draft tokens) is synthesised once,
+untimed, on the GPU; every step draws a fresh Philox offset.
+
+Also reported (``breakdown``): the accept/reject pass alone at B=64, K=7,
+V=128256 bf16 with ragged draft lengths (rotating over 5 input sets, 1.8 GB,
+so the 256 MB Infinity Cache cannot hold them), and the verify GEMM over the
+M = B(1+D) sweep against W [4096, 14336] (rotating over 5 weight copies).
+
+Roofline: the dominant kernel of the step is the lm-head GEMM; its achieved
+bandwidth is its algorithmic bytes (2KN + 2MK + 4MN) over its average launch
+duration, timed with HIP events on the stream it runs on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-breakdown", action="store_true", help="time the step only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["step", "accept", "gemm"], default=None,
+                    help="run one part only (for profiling)")
+    return ap.parse_args()
+
+
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def bench_step(torch, sv, workloads, steps, warmup):
+    dev = torch.device("cuda:0")
+    B, K, V, H = 32, 5, workloads.LMHEAD_N, workloads.HIDDEN
+    M = B * (K + 1)
+    hidden, W = workloads.linear_inputs(M, H, V, seed=5, device=dev)
+    logits = torch.empty(M, V, dtype=torch.float32, device=dev)
+    ws_lin_n = sv.linear_workspace_bytes(M, V, H)
+    ws_lin = torch.empty(max(ws_lin_n, 1), dtype=torch.uint8, device=dev) if ws_lin_n else None
+    sv.verify_linear(hidden, W, out=logits, workspace=ws_lin)
+    z3 = logits.view(B, K + 1, V)
+    g = torch.Generator(device=dev)
+    g.manual_seed(2005)
+    q, x, L = workloads.draft_side_device(z3, K, 1.0, 0.6, g)
+    ws_acc = torch.empty(sv.accept_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+    out = sv.AcceptResult(torch.empty(B, K + 1, dtype=torch.int32, device=dev),
+                          torch.empty(B, dtype=torch.int32, device=dev),
+                          torch.empty(B, K, dtype=torch.float32, device=dev),
+                          torch.empty(B, dtype=torch.int32, device=dev))
+    seed = 0x5EED
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        sv.verify_linear(hidden, W, out=logits, workspace=ws_lin)
+        if ev is not None:
+            ev[1].record()
+        sv.accept(z3, q, x, L, temperature=0.6, seed=seed, offset=i, workspace=ws_acc, out=out)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # pass 1: whole-step throughput, nothing between launches
+    t0, t1 = _events(torch, 2)
+    t0.record()
+    for i in range(steps):
+        step(warmup + i)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_per_step = t0.elapsed_time(t1) / steps
+    # pass 2: the dominant kernel's own duration (events around each launch)
+    evs = [_events(torch, 2) for _ in range(steps)]
+    for i in range(steps):
+        step(warmup + steps + i, evs[i])
+    torch.cuda.synchronize()
+    gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    acc = out.accepted.cpu()
+    emitted = float((acc + 1).float().mean())
+    gemm_bytes = 2 * H * V + 2 * M * H + 4 * M * V
+    gemm_flops = 2 * M * H * V
+    return dict(ms_per_step=ms_per_step, positions=M, gemm_ms=gemm_ms, gemm_bytes=gemm_bytes,
+                gemm_flops=gemm_flops, mean_emitted=emitted,
+                state=dict(hidden=hidden, W=W, logits=logits, q=q, x=x, L=L, B=B, K=K, V=V))
+
+
+def bench_accept_large(torch, sv, workloads, reps=60, nsets=5):
+    dev = torch.device("cuda:0")
+    B, K, V = 64, 7, 128256
+    sets = [workloads.large_accept_device(3000 + s, dev) for s in range(nsets)]
+    ws = torch.empty(sv.accept_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+    outs = [sv.AcceptResult(torch.empty(B, K + 1, dtype=torch.int32, device=dev),
+                            torch.empty(B, dtype=torch.int32, device=dev),
+                            torch.empty(B, K, dtype=torch.float32, device=dev),
+                            torch.empty(B, dtype=torch.int32, device=dev)) for _ in range(nsets)]
+    positions, byts = [], []
+    for s, (z, q, x, L) in enumerate(sets):
+        sv.accept(z, q, x, L, temperature=0.8, seed=77, offset=s, workspace=ws, out=outs[s])
+    torch.cuda.synchronize()
+    for s, (z, q, x, L) in enumerate(sets):
+        Lh = L.cpu().long()
+        a = outs[s].accepted.cpu().long()
+        rows = int((Lh + 1).sum())
+        rej = int((a < Lh).sum())
+        positions.append(rows)
+        # every needed logits row once, one q row per rejecting row, the
+        # token and q(x) gathers, and the outputs
+        byts.append(rows * V * 2 + rej * V * 4 + int(Lh.sum()) * 8 + B * (K + 2) * 4)
+    for r in range(5):
+        for s, (z, q, x, L) in enumerate(sets):
+            sv.accept(z, q, x, L, temperature=0.8, seed=77, offset=s, workspace=ws, out=outs[s])
+    torch.cuda.synchronize()
+    t0, t1 = _events(torch, 2)
+    t0.record()
+    for r in range(reps):
+        for s, (z, q, x, L) in enumerate(sets):
+            sv.accept(z, q, x, L, temperature=0.8, seed=77, offset=s, workspace=ws, out=outs[s])
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / (reps * nsets)
+    pos = sum(positions) / nsets
+    b = sum(byts) / nsets
+    return dict(workload="spec_accept B=64 K=7 V=128256 bf16 T=0.8 ragged L~U{1..7}, 5 rotating sets",
+                us_per_call=us, positions_per_call=pos, positions_per_s=pos / us * 1e6,
+                algorithmic_bytes=b, achieved_GBs=b / us * 1e-3,
+                frac_hbm=b / us * 1e-3 / HBM_PEAK_GBS)
+
+
+def bench_gemm_sweep(torch, sv, workloads, reps=40, ncopies=5):
+    dev = torch.device("cuda:0")
+    H, N = workloads.HIDDEN, workloads.FFN_N
+    Ws = [workloads.linear_inputs(1, H, N, seed=900 + c, device=dev)[1] for c in range(ncopies)]
+    res = []
+    for M in workloads.sweep_ms():
+        X = workloads.linear_inputs(M, H, 8, seed=M, device=dev)[0]
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        need = sv.linear_workspace_bytes(M, N, H)
+        ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+        for c in range(ncopies):
+            sv.verify_linear(X, Ws[c], out=Y, workspace=ws)
+        torch.cuda.synchronize()
+        t0, t1 = _events(torch, 2)
+        t0.record()
+        for r in range(reps):
+            for c in range(ncopies):
+                sv.verify_linear(X, Ws[c], out=Y, workspace=ws)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / (reps * ncopies)
+        byts = 2 * H * N + 2 * M * H + 2 * M * N
+        flops = 2 * M * H * N
+        gbs = byts / us * 1e-3
+        tfl = flops / us * 1e-6
+        res.append(dict(M=M, us=round(us, 2), GBs=round(gbs, 1), TFLOPs=round(tfl, 1),
+                        frac_hbm=round(gbs / HBM_PEAK_GBS, 3),
+                        frac_mfma=round(tfl / BF16_PEAK_TFLOPS, 3)))
+    return dict(workload="spec_verify_linear X[M,4096] x W[4096,14336] bf16 -> bf16, 5 rotating W copies",
+                sweep=res)
+
+
+def cpu_baseline(torch, workloads, st, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the step: the fp64
+    GEMM reference on a column slice of the lm-head (scaled to all columns)
+    plus the fp64 accept/reject oracle on all 32 rows of the step."""
+    import numpy as np
+
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        blas_threads = 1
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    cores = max(1, min(cores, os.cpu_count() or 1))
+    V, B, K = st["V"], st["B"], st["K"]
+    ncols = V // 16
+    Xh = st["hidden"].float().cpu().numpy()
+    Wh = st["W"][:, :ncols].float().cpu().numpy()
+    z = st["logits"].view(B, K + 1, V).cpu().numpy()
+    q = st["q"].cpu().numpy()
+    x = st["x"].cpu().numpy()
+    L = st["L"].cpu().numpy()
+    t_gemm, t_acc, n = 0.0, 0.0, 0
+    t_start = time.perf_counter()
+    while n == 0 or time.perf_counter() - t_start < budget_s:
+        t0 = time.perf_counter()
+        oracle.verify_linear(Xh, Wh)
+        t1 = time.perf_counter()
+        oracle.spec_accept(z, q, x, L, 0.6, 0x5EED, n, nthreads=cores)
+        t2 = time.perf_counter()
+        t_gemm += (t1 - t0) * (V / ncols)
+        t_acc += t2 - t1
+        n += 1
+    per_step = (t_gemm + t_acc) / n
+    return dict(value=round(B * (K + 1) / per_step, 2), unit="verified positions/s",
+                cores=max(cores, blas_threads), kind="oracle",
+                sample=(f"{n} step(s): fp64 numpy GEMM on {ncols} of {V} lm-head columns scaled "
+                        f"x{V / ncols:.0f} ({t_gemm / n:.2f} s/step) + fp64 C accept oracle on all "
+                        f"{B} rows ({t_acc / n:.2f} s/step, {cores} OpenMP threads)"))
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the verification step shards by rows with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import speculative_decoding_verification_accept_amd as sv
+    from speculative_decoding_verification_accept_amd import workloads
+
+    if not os.path.exists(sv.library_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    sv.load_library()
+    torch.cuda.set_device(0)
+
+    if args.only == "accept":
+        print(json.dumps(bench_accept_large(torch, sv, workloads)))
+        return
+    if args.only == "gemm":
+        print(json.dumps(bench_gemm_sweep(torch, sv, workloads)))
+        return
+
+    r = bench_step(torch, sv, workloads, args.steps, args.warmup)
+    ms = r["ms_per_step"]
+    value = r["positions"] / (ms * 1e-3)
+    gemm_gbs = r["gemm_bytes"] / (r["gemm_ms"] * 1e-3) * 1e-9
+    line = {
+        "metric": "verified positions/s (spec_accept) & verify-GEMM TFLOPS; % HBM/MFMA roofline",
+        "value": round(value, 1),
+        "unit": "verified positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; hidden ~ N(0,1), W ~ N(0, 0.02^2), draft logits = target + N(0,1))",
+        "config": {"workload": "fused verify step: lm-head GEMM hidden[192,4096] x W[4096,151936] "
+                               "bf16 -> fp32 logits, then spec_accept B=32 K=5 V=151936 T=0.6",
+                   "B": 32, "K": 5, "V": workloads.LMHEAD_N, "hidden": workloads.HIDDEN,
+                   "M": r["positions"], "parallelism": "single GPU"},
+        "roofline": {"kernel": "spec_verify_linear (lm-head, M=192)", "bound": "hbm",
+                     "achieved": round(gemm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gemm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "avg_launch_us": round(r["gemm_ms"] * 1e3, 2),
+                     "algorithmic_bytes": r["gemm_bytes"],
+                     "tflops": round(r["gemm_flops"] / (r["gemm_ms"] * 1e-3) * 1e-12, 1)},
+        "mean_emitted_per_row": round(r["mean_emitted"], 3),
+    }
+    if not args.no_breakdown:
+        acc = bench_accept_large(torch, sv, workloads)
+        acc = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in acc.items()}
+        line["breakdown"] = {"accept_at_scale": acc,
+                             "gemm_sweep": bench_gemm_sweep(torch, sv, workloads)}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(torch, workloads, r["state"])
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -11,21 +11,23 @@
 // speculative decoding beats it" (trefon.com), section "Speculative
 // decoding" (acceptance rule, greedy longest-prefix rule).
 //
-// Two launches on the caller's stream:
-//  1. k_stats / k_argmax: one workgroup per (row, position <= L_b, chunk of
-//     8192 vocabulary entries).  The chunk is streamed from HBM with 16-byte
-//     coalesced loads into registers, reduced to its max, then to
-//     sum_j 2^(z_j c - fl(m c)) with c = log2(e)/T (one FMA and one v_exp_f32
-//     per element), wave64 shuffles + LDS across the workgroup, fp64 across
-//     waves.  Greedy mode keeps (max, lowest index) instead.
-//  2. k_finish / k_greedy_finish: one workgroup per (row, chunk).  Every
-//     workgroup of a row merges the row's chunk partials (fixed order, fp64),
-//     runs the acceptance tests (p_i(x_i) in fp64) and finds the first
-//     rejection.  After a rejection each workgroup computes the residual mass
-//     of its chunk; the last one to arrive (integer atomic counter) picks the
-//     chunk by a two-level inverse CDF and scans that one chunk in LDS.  A
-//     row with no rejection draws its bonus token from chunk masses it
-//     already has (workgroup 0 of the row).
+// The vocabulary is cut into chunks of 4096 entries.  Three launches on the
+// caller's stream (two in greedy mode); kernel boundaries order the phases,
+// so no workgroup ever waits on, or fences for, another:
+//  1. k_stats: single-wave workgroups walk a compact list of (row, position
+//     <= L_b, chunk) items (the lengths are prefix-summed in registers), each
+//     streaming its 4096 logits from HBM with 16-byte coalesced loads while
+//     the next item's loads are already in flight.  Per chunk: max m, then
+//     sum_j 2^(fl(z_j c - fl(m c))) with c = log2(e)/T (one FMA and one
+//     v_exp_f32 per entry), wave64 butterflies, fp64 across lanes.  Greedy
+//     mode keeps (max, lowest index) instead.
+//  2. k_decide: one workgroup per (row, chunk).  Each merges the row's chunk
+//     partials (fixed order, fp64), runs the acceptance tests (p_i(x_i) in
+//     fp64) and finds the first rejection a_b; after a rejection it computes
+//     the residual mass sum max(p - q, 0) of its chunk.
+//  3. k_sample: one workgroup per row.  Two-level inverse CDF: chunk masses
+//     (residual, or p-frame masses from launch 1 for the bonus token) pick
+//     the chunk, then one LDS-staged fp64 scan of that chunk picks the token.
 // No floating-point atomics: every reduction runs in a fixed order, so the
 // output is a deterministic function of the inputs.
 #include "spec_verify.h"
@@ -37,10 +39,14 @@
 namespace specv {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kEPT = 32;                     // elements per thread per chunk
-constexpr int kChunk = kThreads * kEPT;      // vocabulary entries per chunk
+constexpr int kChunk = 4096;                 // vocabulary entries per chunk
+constexpr int kWEPT = kChunk / kWave;        // entries per lane in k_stats (64)
+constexpr int kThreads = 256;                // k_decide / k_sample workgroups
+constexpr int kTEPT = kChunk / kThreads;     // entries per thread there (16)
 constexpr int kWaves = kThreads / kWave;
+constexpr int kRegLens = 4;                  // lengths held in registers by k_stats
+constexpr int kCompactMaxB = kWave * kRegLens;
+constexpr int kStatsWaves = 4096;            // k_stats grid cap (single-wave workgroups)
 constexpr int kInvalidMask = SPEC_ROW_NONFINITE | SPEC_ROW_BAD_TOKEN | SPEC_ROW_BAD_LEN | SPEC_ROW_ZERO_Q;
 
 struct StatPart {  // stochastic partial of one (row, position, chunk)
@@ -54,21 +60,29 @@ struct ArgPart {  // greedy partial
     int idx;
     int pad;
 };
-static_assert(sizeof(StatPart) == 16 && sizeof(ArgPart) == 16, "partial layout");
+struct RowInfo {  // k_decide -> k_sample
+    int a;        // first rejection (or L_b)
+    int status;   // SPEC_ROW_* bits
+    int reject;   // a < L_b
+    int pad;
+};
+static_assert(sizeof(StatPart) == 16 && sizeof(ArgPart) == 16 && sizeof(RowInfo) == 16, "layout");
 
 typedef uint16_t bf16_t;
 
-// ---- chunk loaders --------------------------------------------------------
-// "Strided" layout: vector k of thread t is vector (k * kThreads + t) of the
-// chunk, so a wave reads consecutive 16-byte vectors (coalesced).  The
-// element index of register e is chunk0 + ((e / W) * kThreads + t) * W + e % W.
+// ---- loaders -----------------------------------------------------------------
+// Vector width (entries per 16-byte load) of each logits layout.
 template <typename T, bool VEC> struct Lay { static constexpr int W = 1; };
 template <> struct Lay<bf16_t, true> { static constexpr int W = 8; };
 template <> struct Lay<float, true> { static constexpr int W = 4; };
 
-template <int W>
+// "Strided" layout over NT threads: vector k of thread t is vector
+// (k * NT + t) of the chunk, so consecutive threads read consecutive 16-byte
+// vectors.  Register e of thread t holds entry
+//   chunk0 + ((e / W) * NT + t) * W + e % W.
+template <int W, int NT>
 __device__ __forceinline__ int64_t strided_index(int64_t chunk0, int t, int e) {
-    return chunk0 + ((int64_t)(e / W) * kThreads + t) * W + (e % W);
+    return chunk0 + ((int64_t)(e / W) * NT + t) * W + (e % W);
 }
 
 __device__ __forceinline__ void unpack8(const uint4 w, float* v) {
@@ -78,53 +92,74 @@ __device__ __forceinline__ void unpack8(const uint4 w, float* v) {
     v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
 }
 
-template <typename T, bool VEC>
-__device__ __forceinline__ void load_strided(const T* row, int64_t V, int64_t chunk0, int t,
-                                             float (&v)[kEPT]) {
-    if constexpr (VEC && sizeof(T) == 2) {
+// One thread's share of a chunk in strided layout, kept as loaded (raw
+// 16-byte vectors) so that loads can stay in flight until the values are used.
+template <typename T, bool VEC, int NT, int EPT> struct Raw;
+
+template <int NT, int EPT> struct Raw<bf16_t, true, NT, EPT> {
+    uint4 r[EPT / 8];
+    __device__ __forceinline__ void load(const bf16_t* row, int64_t V, int64_t chunk0, int t) {
         const uint4* p = reinterpret_cast<const uint4*>(row);
-        const uint4 ninf = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
-        uint4 w[kEPT / 8];
 #pragma unroll
-        for (int k = 0; k < kEPT / 8; ++k) {
-            const int64_t vi = chunk0 / 8 + (int64_t)k * kThreads + t;
-            w[k] = (vi * 8 < V) ? p[vi] : ninf;
+        for (int k = 0; k < EPT / 8; ++k) {
+            const int64_t vi = chunk0 / 8 + (int64_t)k * NT + t;
+            r[k] = (vi * 8 < V) ? p[vi] : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
         }
+    }
+    __device__ __forceinline__ void unpack(float (&v)[EPT]) const {
 #pragma unroll
-        for (int k = 0; k < kEPT / 8; ++k) unpack8(w[k], v + 8 * k);
-    } else if constexpr (VEC) {
+        for (int k = 0; k < EPT / 8; ++k) unpack8(r[k], v + 8 * k);
+    }
+};
+
+template <int NT, int EPT> struct Raw<float, true, NT, EPT> {
+    float4 r[EPT / 4];
+    __device__ __forceinline__ void load(const float* row, int64_t V, int64_t chunk0, int t) {
         const float4* p = reinterpret_cast<const float4*>(row);
-        const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
 #pragma unroll
-        for (int k = 0; k < kEPT / 4; ++k) {
-            const int64_t vi = chunk0 / 4 + (int64_t)k * kThreads + t;
-            const float4 f = (vi * 4 < V) ? p[vi] : ninf;
-            v[4 * k] = f.x; v[4 * k + 1] = f.y; v[4 * k + 2] = f.z; v[4 * k + 3] = f.w;
+        for (int k = 0; k < EPT / 4; ++k) {
+            const int64_t vi = chunk0 / 4 + (int64_t)k * NT + t;
+            r[k] = (vi * 4 < V) ? p[vi] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         }
-    } else {
+    }
+    __device__ __forceinline__ void unpack(float (&v)[EPT]) const {
 #pragma unroll
-        for (int e = 0; e < kEPT; ++e) {
-            const int64_t j = chunk0 + (int64_t)e * kThreads + t;
+        for (int k = 0; k < EPT / 4; ++k) {
+            v[4 * k] = r[k].x; v[4 * k + 1] = r[k].y; v[4 * k + 2] = r[k].z; v[4 * k + 3] = r[k].w;
+        }
+    }
+};
+
+template <typename T, int NT, int EPT> struct Raw<T, false, NT, EPT> {
+    float r[EPT];
+    __device__ __forceinline__ void load(const T* row, int64_t V, int64_t chunk0, int t) {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            const int64_t j = chunk0 + (int64_t)e * NT + t;
             float x = -INFINITY;
             if (j < V) {
                 if constexpr (sizeof(T) == 2) x = bf16_to_f32(row[j]);
                 else x = row[j];
             }
-            v[e] = x;
+            r[e] = x;
         }
     }
-}
+    __device__ __forceinline__ void unpack(float (&v)[EPT]) const {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) v[e] = r[e];
+    }
+};
 
-// q values matching load_strided<T, VEC>'s element order; 0 past V.
-template <typename T, bool VEC>
+// q entries in the same order as Raw<T, VEC, NT, EPT>; 0 past V.
+template <typename T, bool VEC, int NT, int EPT>
 __device__ __forceinline__ void load_q_strided(const float* row, int64_t V, int64_t chunk0, int t,
-                                               float (&v)[kEPT]) {
+                                               float (&v)[EPT]) {
     constexpr int W = Lay<T, VEC>::W;
     if constexpr (W > 1) {
         const float4* p = reinterpret_cast<const float4*>(row);
 #pragma unroll
-        for (int k = 0; k < kEPT / W; ++k) {
-            const int64_t vi = chunk0 / W + (int64_t)k * kThreads + t;
+        for (int k = 0; k < EPT / W; ++k) {
+            const int64_t vi = chunk0 / W + (int64_t)k * NT + t;
 #pragma unroll
             for (int h = 0; h < W / 4; ++h) {
                 const float4 f = (vi * W < V) ? p[vi * (W / 4) + h] : make_float4(0.f, 0.f, 0.f, 0.f);
@@ -134,35 +169,34 @@ __device__ __forceinline__ void load_q_strided(const float* row, int64_t V, int6
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < kEPT; ++e) {
-            const int64_t j = chunk0 + (int64_t)e * kThreads + t;
+        for (int e = 0; e < EPT; ++e) {
+            const int64_t j = chunk0 + (int64_t)e * NT + t;
             v[e] = (j < V) ? row[j] : 0.f;
         }
     }
 }
 
-// "Contiguous" layout for the in-chunk scan: thread t owns entries
-// [start + t*kEPT, start + (t+1)*kEPT) in order.
-template <typename T, bool VEC>
-__device__ __forceinline__ void load_contig(const T* row, int64_t V, int64_t start, float (&v)[kEPT]) {
+// "Contiguous" layout for the in-chunk scan: the thread owns entries
+// [start, start + EPT) in order.
+template <typename T, bool VEC, int EPT>
+__device__ __forceinline__ void load_contig(const T* row, int64_t V, int64_t start, float (&v)[EPT]) {
     if constexpr (VEC && sizeof(T) == 2) {
         const uint4* p = reinterpret_cast<const uint4*>(row + start);
-        const uint4 ninf = make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
 #pragma unroll
-        for (int k = 0; k < kEPT / 8; ++k) {
-            const uint4 w = (start + 8 * k < V) ? p[k] : ninf;
+        for (int k = 0; k < EPT / 8; ++k) {
+            const uint4 w = (start + 8 * k < V) ? p[k] : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
             unpack8(w, v + 8 * k);
         }
     } else if constexpr (VEC) {
         const float4* p = reinterpret_cast<const float4*>(row + start);
 #pragma unroll
-        for (int k = 0; k < kEPT / 4; ++k) {
+        for (int k = 0; k < EPT / 4; ++k) {
             const float4 f = (start + 4 * k < V) ? p[k] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
             v[4 * k] = f.x; v[4 * k + 1] = f.y; v[4 * k + 2] = f.z; v[4 * k + 3] = f.w;
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < kEPT; ++e) {
+        for (int e = 0; e < EPT; ++e) {
             const int64_t j = start + e;
             float x = -INFINITY;
             if (j < V) {
@@ -174,18 +208,18 @@ __device__ __forceinline__ void load_contig(const T* row, int64_t V, int64_t sta
     }
 }
 
-template <bool VEC>
-__device__ __forceinline__ void load_q_contig(const float* row, int64_t V, int64_t start, float (&v)[kEPT]) {
+template <bool VEC, int EPT>
+__device__ __forceinline__ void load_q_contig(const float* row, int64_t V, int64_t start, float (&v)[EPT]) {
     if constexpr (VEC) {
         const float4* p = reinterpret_cast<const float4*>(row + start);
 #pragma unroll
-        for (int k = 0; k < kEPT / 4; ++k) {
+        for (int k = 0; k < EPT / 4; ++k) {
             const float4 f = (start + 4 * k < V) ? p[k] : make_float4(0.f, 0.f, 0.f, 0.f);
             v[4 * k] = f.x; v[4 * k + 1] = f.y; v[4 * k + 2] = f.z; v[4 * k + 3] = f.w;
         }
     } else {
 #pragma unroll
-        for (int e = 0; e < kEPT; ++e) v[e] = (start + e < V) ? row[start + e] : 0.f;
+        for (int e = 0; e < EPT; ++e) v[e] = (start + e < V) ? row[start + e] : 0.f;
     }
 }
 
@@ -195,7 +229,7 @@ __device__ __forceinline__ float load_one(const T* row, int64_t j) {
     else return row[j];
 }
 
-// ---- per-element weights (identical expressions wherever used) -----------
+// ---- per-entry weights (identical expressions wherever used) -----------------
 // p-frame weight of logit z at a position with fl(M c) = mc.
 __device__ __forceinline__ float p_weight(float z, float c, float mc) {
     return hw_exp2(__builtin_fmaf(z, c, -mc));
@@ -206,19 +240,14 @@ __device__ __forceinline__ float r_weight(float z, float q, float c, float mc, f
     return fmaxf(p - q, 0.f);
 }
 
-// ---- workgroup reductions -------------------------------------------------
-__device__ __forceinline__ float block_max(float v, float* sh) {
-    v = wave_max(v);
-    const int w = threadIdx.x / kWave;
-    if ((threadIdx.x & (kWave - 1)) == 0) sh[w] = v;
-    __syncthreads();
-    float r = sh[0];
-#pragma unroll
-    for (int k = 1; k < kWaves; ++k) r = fmaxf(r, sh[k]);
-    __syncthreads();
-    return r;
+// p-frame mass of one chunk partial relative to the position's fl(M c).
+__device__ __forceinline__ double chunk_p_mass(const StatPart& e, float c, float mcM) {
+    if (e.m == -INFINITY) return 0.0;
+    const float mck = e.m * c;
+    return e.s * exp2((double)mck - (double)mcM);
 }
 
+// ---- workgroup reductions -------------------------------------------------------
 __device__ __forceinline__ double block_sum(double v, double* sh) {
     v = wave_sum(v);
     const int w = threadIdx.x / kWave;
@@ -231,360 +260,463 @@ __device__ __forceinline__ double block_sum(double v, double* sh) {
     return r;
 }
 
-__device__ __forceinline__ int block_or(int v, int* sh) {
-    v = wave_or(v);
-    const int w = threadIdx.x / kWave;
-    if ((threadIdx.x & (kWave - 1)) == 0) sh[w] = v;
-    __syncthreads();
-    int r = 0;
+// Inclusive scan of one double per thread across the workgroup (wave64
+// shuffle scan, then the wave totals in order); also returns the total.
+__device__ __forceinline__ double block_incl_scan(double v, double* sh, double* total) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wv = threadIdx.x / kWave;
 #pragma unroll
-    for (int k = 0; k < kWaves; ++k) r |= sh[k];
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double n = __shfl_up(v, o, kWave);
+        if (lane >= o) v += n;
+    }
+    if (lane == kWave - 1) sh[wv] = v;
     __syncthreads();
-    return r;
+    double base = 0.0, tot = 0.0;
+#pragma unroll
+    for (int k = 0; k < kWaves; ++k) {
+        if (k < wv) base += sh[k];
+        tot += sh[k];
+    }
+    __syncthreads();
+    *total = tot;
+    return base + v;
 }
 
-// ---- launch 1: chunk statistics --------------------------------------------
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_stats(const T* __restrict__ logits,
-                                                    const int32_t* __restrict__ lens, int K,
-                                                    int64_t V, int C, float c,
-                                                    StatPart* __restrict__ part,
-                                                    int32_t* __restrict__ counters) {
-    __shared__ float sh_f[kWaves];
-    __shared__ double sh_d[kWaves];
-    __shared__ int sh_i[kWaves];
-    const int64_t bid = blockIdx.x;
-    const int ci = (int)(bid % C);
-    const int64_t rp = bid / C;
-    const int i = (int)(rp % (K + 1));
-    const int64_t b = rp / (K + 1);
-    const int t = threadIdx.x;
-    if (i == 0 && ci == 0 && t == 0) counters[b] = 0;
-    const int L = lens ? lens[b] : K;
-    if (L < 0 || L > K || i > L) return;
-
-    float v[kEPT];
-    load_strided<T, VEC>(logits + rp * V, V, (int64_t)ci * kChunk, t, v);
-
-    float m = -INFINITY;
+__device__ __forceinline__ int wave_incl_scan_int(int v) {
+    const int lane = threadIdx.x & (kWave - 1);
 #pragma unroll
-    for (int e = 0; e < kEPT; ++e) m = fmaxf(m, v[e]);
-    m = block_max(m, sh_f);
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int n = __shfl_up(v, o, kWave);
+        if (lane >= o) v += n;
+    }
+    return v;
+}
 
+// Merge of the C chunk partials of one position by one wave (lanes over
+// chunks, butterfly reductions: a fixed order).  Every kernel that needs a
+// position's (M, S) calls this, so they all see the same bits.
+struct PosStats {
+    float M;
+    double S;
+    int flag;
+};
+__device__ __forceinline__ PosStats merge_position(const StatPart* pp, int C, float c) {
+    const int lane = threadIdx.x & (kWave - 1);
+    float M = -INFINITY;
     int flag = 0;
-    double s = 0.0;
-    if (m == INFINITY) {
-        flag = 1;
-    } else if (m == -INFINITY) {
-        int nan = 0;
-#pragma unroll
-        for (int e = 0; e < kEPT; ++e) nan |= (v[e] != v[e]);
-        flag = block_or(nan, sh_i);
-    } else {
-        const float mc = m * c;
-        float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
-#pragma unroll
-        for (int e = 0; e < kEPT; e += 4) {
-            a0 += p_weight(v[e], c, mc);
-            a1 += p_weight(v[e + 1], c, mc);
-            a2 += p_weight(v[e + 2], c, mc);
-            a3 += p_weight(v[e + 3], c, mc);
-        }
-        s = block_sum((double)((a0 + a1) + (a2 + a3)), sh_d);
-        flag = (s != s) ? 1 : 0;
+    for (int k = lane; k < C; k += kWave) {
+        M = fmaxf(M, pp[k].m);
+        flag |= pp[k].flag;
     }
-    if (t == 0) part[bid] = StatPart{m, flag, s};
+    M = wave_max(M);
+    flag = wave_or(flag);
+    if (M == -INFINITY || M == INFINITY) flag = 1;
+    const float mcM = M * c;
+    double S = 0.0;
+    if (!flag)
+        for (int k = lane; k < C; k += kWave) S += chunk_p_mass(pp[k], c, mcM);
+    S = wave_sum(S);
+    return PosStats{M, S, flag};
 }
 
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_argmax(const T* __restrict__ logits,
-                                                     const int32_t* __restrict__ lens, int K,
-                                                     int64_t V, int C, ArgPart* __restrict__ part) {
-    __shared__ float sh_v[kWaves];
-    __shared__ int sh_x[kWaves];
-    __shared__ int sh_f[kWaves];
-    const int64_t bid = blockIdx.x;
-    const int ci = (int)(bid % C);
-    const int64_t rp = bid / C;
-    const int i = (int)(rp % (K + 1));
-    const int64_t b = rp / (K + 1);
-    const int t = threadIdx.x;
-    const int L = lens ? lens[b] : K;
-    if (L < 0 || L > K || i > L) return;
+// ---- launch 1: chunk statistics ----------------------------------------------------
+// Work list of (row-position rp = b (K+1) + i, chunk).  For B <= 256 the
+// list is compact: lane l holds n_b = L_b + 1 (0 for a bad length) for
+// b = l + 64 j, prefix-summed across the wave, and item w maps to
+// position pos = w / C of the concatenated valid positions.  Larger batches
+// walk all B (K+1) positions and skip those past L_b.
+struct WorkList {
+    int pst[kRegLens];  // exclusive prefix of n_b, b = lane + 64 j
+    int64_t B;
+    int K, C;
+    bool compact;
+    const int32_t* lens;
+    int64_t nitems;
 
-    float v[kEPT];
-    const int64_t chunk0 = (int64_t)ci * kChunk;
-    load_strided<T, VEC>(logits + rp * V, V, chunk0, t, v);
+    __device__ __forceinline__ void init(const int32_t* lens_, int64_t B_, int K_, int C_) {
+        lens = lens_;
+        B = B_;
+        K = K_;
+        C = C_;
+        compact = B <= kCompactMaxB;
+        if (compact) {
+            const int lane = threadIdx.x & (kWave - 1);
+            int carry = 0;
+#pragma unroll
+            for (int j = 0; j < kRegLens; ++j) {
+                const int64_t b = lane + kWave * j;
+                int n = 0;
+                if (b < B) {
+                    const int L = lens ? lens[b] : K;
+                    n = (L >= 0 && L <= K) ? L + 1 : 0;
+                }
+                const int incl = wave_incl_scan_int(n);
+                pst[j] = carry + incl - n;
+                carry += __shfl(incl, kWave - 1, kWave);
+            }
+            nitems = (int64_t)carry * C;
+        } else {
+            nitems = B * (K + 1) * C;
+        }
+    }
+    // item w -> (rp, chunk); false if the item is past L_b (non-compact only)
+    __device__ __forceinline__ bool locate(int64_t w, int64_t& rp, int& ci) const {
+        const int64_t pos = w / C;
+        ci = (int)(w % C);
+        if (compact) {
+            const int lane = threadIdx.x & (kWave - 1);
+            int cnt = 0;
+#pragma unroll
+            for (int j = 0; j < kRegLens; ++j)
+                cnt += __popcll(__ballot((lane + kWave * j < B) && (int64_t)pst[j] <= pos));
+            const int b = cnt - 1;
+            const int j = b / kWave;
+            static_assert(kRegLens == 4, "select chain below");
+            const int sel = (j == 0) ? pst[0] : (j == 1) ? pst[1] : (j == 2) ? pst[2] : pst[3];
+            const int base = __shfl(sel, b % kWave, kWave);
+            rp = (int64_t)b * (K + 1) + (pos - base);
+            return true;
+        }
+        rp = pos;
+        const int64_t b = rp / (K + 1);
+        const int i = (int)(rp % (K + 1));
+        const int L = lens ? lens[b] : K;
+        return L >= 0 && L <= K && i <= L;
+    }
+    // first valid item at or after w in steps of `stride`
+    __device__ __forceinline__ bool next(int64_t& w, int64_t stride, int64_t& rp, int& ci) const {
+        while (w < nitems) {
+            if (locate(w, rp, ci)) return true;
+            w += stride;
+        }
+        return false;
+    }
+};
+
+template <typename T, bool VEC, bool GREEDY>
+__global__ __launch_bounds__(kWave) void k_stats(const T* __restrict__ logits,
+                                                 const int32_t* __restrict__ lens, int64_t B, int K,
+                                                 int64_t V, int C, float c, void* __restrict__ part_out) {
     constexpr int W = Lay<T, VEC>::W;
-    float best = -INFINITY;
-    int bidx = 0x7FFFFFFF;
-    int nan = 0;
+    const int lane = threadIdx.x;
+    WorkList wl;
+    wl.init(lens, B, K, C);
+    const int64_t stride = gridDim.x;
+    int64_t w = blockIdx.x, rp = 0;
+    int ci = 0;
+    bool have = wl.next(w, stride, rp, ci);
+    Raw<T, VEC, kWave, kWEPT> cur;
+    if (have) cur.load(logits + rp * V, V, (int64_t)ci * kChunk, lane);
+    while (have) {
+        // issue the next item's loads before reducing this one
+        int64_t wn = w + stride, rpn = 0;
+        int cin = 0;
+        const bool haven = wl.next(wn, stride, rpn, cin);
+        Raw<T, VEC, kWave, kWEPT> nxt;
+        if (haven) nxt.load(logits + rpn * V, V, (int64_t)cin * kChunk, lane);
+
+        float v[kWEPT];
+        cur.unpack(v);
+        const int64_t pidx = rp * C + ci;
+        if constexpr (GREEDY) {
+            const int64_t chunk0 = (int64_t)ci * kChunk;
+            float best = -INFINITY;
+            int bidx = 0x7FFFFFFF, nan = 0;
 #pragma unroll
-    for (int e = 0; e < kEPT; ++e) {
-        const int64_t j = strided_index<W>(chunk0, t, e);
-        const float x = v[e];
-        if (j < V) {
-            nan |= (x != x);
-            if (x > best || (x == best && (int)j < bidx)) { best = x; bidx = (int)j; }
-        }
-    }
-    // wave then workgroup reduction of (max, lowest index)
+            for (int e = 0; e < kWEPT; ++e) {
+                const int64_t j = strided_index<W, kWave>(chunk0, lane, e);
+                const float x = v[e];
+                if (j < V) {
+                    nan |= (x != x);
+                    if (x > best || (x == best && (int)j < bidx)) { best = x; bidx = (int)j; }
+                }
+            }
 #pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(best, o, kWave);
-        const int oi = __shfl_xor(bidx, o, kWave);
-        if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
-    }
-    nan = wave_or(nan);
-    const int w = t / kWave;
-    if ((t & (kWave - 1)) == 0) { sh_v[w] = best; sh_x[w] = bidx; sh_f[w] = nan; }
-    __syncthreads();
-    if (t == 0) {
-        float bv = sh_v[0];
-        int bi = sh_x[0];
-        int f = sh_f[0];
-        for (int k = 1; k < kWaves; ++k) {
-            if (sh_v[k] > bv || (sh_v[k] == bv && sh_x[k] < bi)) { bv = sh_v[k]; bi = sh_x[k]; }
-            f |= sh_f[k];
+            for (int o = kWave / 2; o > 0; o >>= 1) {
+                const float ov = __shfl_xor(best, o, kWave);
+                const int oi = __shfl_xor(bidx, o, kWave);
+                if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
+            }
+            nan = wave_or(nan);
+            if (lane == 0)
+                static_cast<ArgPart*>(part_out)[pidx] = ArgPart{best, (nan || best == INFINITY) ? 1 : 0, bidx, 0};
+        } else {
+            float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < kWEPT; e += 2) {
+                m0 = fmaxf(m0, v[e]);
+                m1 = fmaxf(m1, v[e + 1]);
+            }
+            const float m = wave_max(fmaxf(m0, m1));
+            int flag = 0;
+            double s = 0.0;
+            if (m == INFINITY) {
+                flag = 1;
+            } else if (m == -INFINITY) {
+                int nan = 0;
+#pragma unroll
+                for (int e = 0; e < kWEPT; ++e) nan |= (v[e] != v[e]);
+                flag = wave_or(nan);
+            } else {
+                const float mc = m * c;
+                float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+                for (int e = 0; e < kWEPT; e += 4) {
+                    a0 += p_weight(v[e], c, mc);
+                    a1 += p_weight(v[e + 1], c, mc);
+                    a2 += p_weight(v[e + 2], c, mc);
+                    a3 += p_weight(v[e + 3], c, mc);
+                }
+                s = wave_sum((double)((a0 + a1) + (a2 + a3)));
+                flag = (s != s) ? 1 : 0;
+            }
+            if (lane == 0) static_cast<StatPart*>(part_out)[pidx] = StatPart{m, flag, s};
         }
-        if (bv == INFINITY) f = 1;
-        part[bid] = ArgPart{bv, f, bi, 0};
+        cur = nxt;
+        w = wn;
+        rp = rpn;
+        ci = cin;
+        have = haven;
     }
 }
 
-// ---- launch 2: decisions, residual masses and the draw ----------------------
+// ---- launch 2: decisions and residual chunk masses ----------------------------------
 template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_finish(
+__global__ __launch_bounds__(kThreads) void k_decide(
     const T* __restrict__ logits, const float* __restrict__ q, const int32_t* __restrict__ tokens,
     const int32_t* __restrict__ lens, int K, int64_t V, int C, float c, int64_t row_base,
-    uint64_t seed, uint64_t offset, const StatPart* __restrict__ part, double* resid,
-    int32_t* counters, int32_t* __restrict__ out_tokens, int32_t* __restrict__ out_accepted,
-    float* __restrict__ out_p_draft, int32_t* __restrict__ out_status) {
-    __shared__ float s_M[SPEC_MAX_DRAFT + 1];
-    __shared__ double s_S[SPEC_MAX_DRAFT + 1];
-    __shared__ int s_acc[SPEC_MAX_DRAFT + 1];
-    __shared__ float s_px[SPEC_MAX_DRAFT + 1];
+    uint64_t seed, uint64_t offset, const StatPart* __restrict__ part, double* __restrict__ resid,
+    RowInfo* __restrict__ info, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ out_accepted, float* __restrict__ out_p_draft,
+    int32_t* __restrict__ out_status) {
+    constexpr int kPos = SPEC_MAX_DRAFT + 1;
+    __shared__ float s_M[kPos];
+    __shared__ double s_S[kPos];
+    __shared__ int s_flag[kPos];
+    __shared__ float s_zx[kPos];
+    __shared__ float s_qx[kPos];
+    __shared__ float s_px[kPos];
     __shared__ double sh_d[kWaves];
-    __shared__ double s_scan[kThreads + 1];
-    __shared__ int s_status, s_a, s_last, s_cstar, s_pmode, s_tok, s_lastpos;
-    __shared__ double s_tp;
+    __shared__ int s_status, s_a;
 
     const int64_t b = blockIdx.x / C;
     const int ci = (int)(blockIdx.x % C);
     const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wv = t / kWave;
     const int L = lens ? lens[b] : K;
     const bool len_ok = (L >= 0 && L <= K);
     if (t == 0) {
         s_status = len_ok ? 0 : SPEC_ROW_BAD_LEN;
-        s_tok = 0x7FFFFFFF;
-        s_lastpos = -1;
+        s_a = len_ok ? L : 0;
     }
     __syncthreads();
 
-    // Merge the chunk partials of every position <= L_b and test each draft.
+    // gather z_i(x_i) and q_i(x_i) of every drafted position (one thread each)
+    if (len_ok && t < L) {
+        const int x = tokens[b * K + t];
+        int st = 0;
+        float zx = 0.f, qx = 1.f;
+        if (x < 0 || (int64_t)x >= V) {
+            st = SPEC_ROW_BAD_TOKEN;
+        } else {
+            zx = load_one(logits + (b * (K + 1) + t) * V, x);
+            qx = q[(b * K + t) * V + x];
+            if (!(qx > 0.f)) st = SPEC_ROW_ZERO_Q;
+        }
+        s_zx[t] = zx;
+        s_qx[t] = qx;
+        if (st) atomicOr(&s_status, st);
+    }
+    // merge the chunk partials of each position <= L_b, one wave per position
     if (len_ok) {
-        for (int i = t; i <= L; i += kThreads) {
-            const StatPart* pp = part + ((b * (K + 1) + i) * C);
-            float M = -INFINITY;
-            int flag = 0;
-            for (int k = 0; k < C; ++k) { M = fmaxf(M, pp[k].m); flag |= pp[k].flag; }
-            if (M == -INFINITY || M == INFINITY) flag = 1;
-            const float mcM = M * c;
-            double S = 0.0;
-            if (!flag)
-                for (int k = 0; k < C; ++k) {
-                    const StatPart e = pp[k];
-                    if (e.m != -INFINITY) {
-                        const float mck = e.m * c;
-                        S += e.s * exp2((double)mck - (double)mcM);
-                    }
-                }
-            s_M[i] = M;
-            s_S[i] = S;
-            int st = flag ? SPEC_ROW_NONFINITE : 0;
-            int acc = 1;
-            float px = -1.f;
-            if (i < L) {
-                const int x = tokens[b * K + i];
-                if (x < 0 || (int64_t)x >= V) {
-                    st |= SPEC_ROW_BAD_TOKEN;
-                } else {
-                    const float qx = q[(b * K + i) * V + x];
-                    if (!(qx > 0.f)) st |= SPEC_ROW_ZERO_Q;
-                    if (!flag) {
-                        const double zx = (double)load_one(logits + (b * (K + 1) + i) * V, x);
-                        const double p = exp2(zx * (double)c - (double)mcM) / S;
-                        px = (float)p;
-                        if (qx > 0.f) {
-                            const double a = fmin(1.0, p / (double)qx);
-                            const RowPosUniforms u = row_pos_uniforms(seed, offset, (uint32_t)(row_base + b), (uint32_t)i);
-                            acc = ((double)u.acc < a) ? 1 : 0;
-                        }
-                    }
-                }
+        for (int i = wv; i <= L; i += kWaves) {
+            const PosStats ps = merge_position(part + (b * (K + 1) + i) * C, C, c);
+            if (lane == 0) {
+                s_M[i] = ps.M;
+                s_S[i] = ps.S;
+                s_flag[i] = ps.flag;
+                if (ps.flag) atomicOr(&s_status, SPEC_ROW_NONFINITE);
             }
-            s_acc[i] = acc;
-            s_px[i] = px;
-            if (st) atomicOr(&s_status, st);
         }
     }
     __syncthreads();
-    if (t == 0) {
-        int a = L;
-        if (len_ok)
-            for (int i = 0; i < L; ++i)
-                if (!s_acc[i]) { a = i; break; }
-        s_a = a;
+    // acceptance tests, then the first rejection
+    if (len_ok && t < L) {
+        float px = -1.f;
+        int rej = 0;
+        const float qx = s_qx[t];
+        if (!s_flag[t] && qx > 0.f) {
+            const float mcM = s_M[t] * c;
+            const double p = exp2((double)s_zx[t] * (double)c - (double)mcM) / s_S[t];
+            px = (float)p;
+            const double a = fmin(1.0, p / (double)qx);
+            const RowPosUniforms u = row_pos_uniforms(seed, offset, (uint32_t)(row_base + b), (uint32_t)t);
+            rej = ((double)u.acc < a) ? 0 : 1;
+        }
+        s_px[t] = px;
+        if (rej) atomicMin(&s_a, t);
     }
     __syncthreads();
-    int status = s_status;
+    const int status = s_status;
     const int a = s_a;
     const bool invalid = (status & kInvalidMask) != 0;
-    if (ci == 0 && out_p_draft)
-        for (int i = t; i < K; i += kThreads)
-            out_p_draft[b * K + i] = (!invalid && i < L) ? s_px[i] : -1.f;
-    if (invalid) {
-        if (ci == 0) {
+    const bool reject = !invalid && a < L;
+    if (ci == 0) {
+        if (out_p_draft)
+            for (int i = t; i < K; i += kThreads)
+                out_p_draft[b * K + i] = (!invalid && i < L) ? s_px[i] : -1.f;
+        if (invalid) {
             for (int i = t; i <= K; i += kThreads) out_tokens[b * (K + 1) + i] = -1;
             if (t == 0) {
                 out_accepted[b] = -1;
                 if (out_status) out_status[b] = status;
             }
         }
-        return;
+        if (t == 0) info[b] = RowInfo{a, status, reject ? 1 : 0, 0};
     }
+    if (!reject) return;
 
-    const bool reject = a < L;
-    const float M = s_M[a];
-    const double S = s_S[a];
-    const float mcM = M * c;
-    const float invS = (float)(1.0 / S);
+    // residual mass of this chunk at the rejected position
+    const float mcM = s_M[a] * c;
+    const float invS = (float)(1.0 / s_S[a]);
     const T* zrow = logits + (b * (K + 1) + a) * V;
-    const float* qrow = reject ? q + (b * K + a) * V : nullptr;
-
-    if (reject) {
-        // residual mass of this chunk
-        float z[kEPT], qq[kEPT];
-        const int64_t chunk0 = (int64_t)ci * kChunk;
-        load_strided<T, VEC>(zrow, V, chunk0, t, z);
-        load_q_strided<T, VEC>(qrow, V, chunk0, t, qq);
-        float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
+    const float* qrow = q + (b * K + a) * V;
+    const int64_t chunk0 = (int64_t)ci * kChunk;
+    Raw<T, VEC, kThreads, kTEPT> raw;
+    raw.load(zrow, V, chunk0, t);
+    float qq[kTEPT], z[kTEPT];
+    load_q_strided<T, VEC, kThreads, kTEPT>(qrow, V, chunk0, t, qq);
+    raw.unpack(z);
+    float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
 #pragma unroll
-        for (int e = 0; e < kEPT; e += 4) {
-            r0 += r_weight(z[e], qq[e], c, mcM, invS);
-            r1 += r_weight(z[e + 1], qq[e + 1], c, mcM, invS);
-            r2 += r_weight(z[e + 2], qq[e + 2], c, mcM, invS);
-            r3 += r_weight(z[e + 3], qq[e + 3], c, mcM, invS);
-        }
-        const double R = block_sum((double)((r0 + r1) + (r2 + r3)), sh_d);
-        if (t == 0) {
-            __hip_atomic_store(&resid[b * C + ci], R, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __threadfence();
-            const int old = atomicAdd(&counters[b], 1);
-            s_last = (old == C - 1) ? 1 : 0;
-        }
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();
-    } else if (ci != 0) {
-        return;
+    for (int e = 0; e < kTEPT; e += 4) {
+        r0 += r_weight(z[e], qq[e], c, mcM, invS);
+        r1 += r_weight(z[e + 1], qq[e + 1], c, mcM, invS);
+        r2 += r_weight(z[e + 2], qq[e + 2], c, mcM, invS);
+        r3 += r_weight(z[e + 3], qq[e + 3], c, mcM, invS);
     }
+    const double R = block_sum((double)((r0 + r1) + (r2 + r3)), sh_d);
+    if (t == 0) resid[b * C + ci] = R;
+}
 
-    // Pick the chunk (first level of the inverse CDF).
-    if (t == 0) {
-        const RowPosUniforms u = row_pos_uniforms(seed, offset, (uint32_t)(row_base + b), (uint32_t)a);
-        int pmode = reject ? 0 : 1;
-        double tot = 0.0;
-        if (reject) {
-            for (int k = 0; k < C; ++k)
-                tot += __hip_atomic_load(&resid[b * C + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (!(tot > 0.0)) { pmode = 1; status |= SPEC_ROW_RESID_ZERO; }
+// ---- launch 3: the categorical draw ------------------------------------------------------
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kThreads) void k_sample(
+    const T* __restrict__ logits, const float* __restrict__ q, const int32_t* __restrict__ tokens,
+    int K, int64_t V, int C, float c, int64_t row_base, uint64_t seed, uint64_t offset,
+    const StatPart* __restrict__ part, const double* __restrict__ resid,
+    const RowInfo* __restrict__ info, int32_t* __restrict__ out_tokens,
+    int32_t* __restrict__ out_accepted, int32_t* __restrict__ out_status) {
+    __shared__ double sh_d[kWaves];
+    __shared__ double s_scan[kThreads + 1];
+    __shared__ float s_M;
+    __shared__ double s_S, s_tp;
+    __shared__ int s_cstar, s_tok, s_lastpos;
+
+    const int64_t b = blockIdx.x;
+    const int t = threadIdx.x;
+    const RowInfo ri = info[b];
+    if (ri.status & kInvalidMask) return;  // k_decide wrote this row
+    const int a = ri.a;
+    int status = ri.status;
+    const StatPart* pp = part + (b * (K + 1) + a) * C;
+    if (t < kWave) {
+        const PosStats ps = merge_position(pp, C, c);
+        if (t == 0) {
+            s_M = ps.M;
+            s_S = ps.S;
+            s_cstar = 0x7FFFFFFF;
+            s_tok = 0x7FFFFFFF;
+            s_lastpos = -1;
         }
-        const StatPart* pp = part + ((b * (K + 1) + a) * C);
-        auto chunk_w = [&](int k) -> double {
-            if (!pmode) return __hip_atomic_load(&resid[b * C + k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const StatPart e = pp[k];
-            if (e.m == -INFINITY) return 0.0;
-            const float mck = e.m * c;
-            return e.s * exp2((double)mck - (double)mcM);
-        };
-        if (pmode) {
-            tot = 0.0;
-            for (int k = 0; k < C; ++k) tot += chunk_w(k);
-        }
-        const double tt = (double)u.smp * tot;
-        double cum = 0.0;
-        int cstar = -1, lastpos = -1;
-        double before = 0.0;
-        for (int k = 0; k < C; ++k) {
-            const double wk = chunk_w(k);
-            if (wk > 0.0) lastpos = k;
-            if (cstar < 0 && cum + wk > tt) { cstar = k; before = cum; }
-            cum += wk;
-        }
-        double tp = tt - before;
-        if (cstar < 0) {  // rounding left t at or past the total: last positive entry overall
-            cstar = lastpos;
-            tp = INFINITY;
-        }
-        s_cstar = cstar;
-        s_pmode = pmode;
-        s_tp = tp;
-        s_status = status;
     }
     __syncthreads();
-    const int cstar = s_cstar;
-    const int pmode = s_pmode;
-    const double tp = s_tp;
-    status = s_status;
+    const float mcM = s_M * c;
+    const float invS = (float)(1.0 / s_S);
+    const T* zrow = logits + (b * (K + 1) + a) * V;
+    const float* qrow = ri.reject ? q + (b * K + a) * V : nullptr;
 
-    // Second level: scan the chosen chunk in index order.
-    const int64_t start = (int64_t)cstar * kChunk + (int64_t)t * kEPT;
-    float w[kEPT];
+    // first level: pick the chunk from the chunk masses
+    int pmode = ri.reject ? 0 : 1;
+    auto chunk_w = [&](int k) -> double {
+        if (k >= C) return 0.0;
+        return pmode ? chunk_p_mass(pp[k], c, mcM) : resid[b * C + k];
+    };
+    double tot = 0.0;
+    for (int k0 = 0; k0 < C; k0 += kThreads) tot += block_sum(chunk_w(k0 + t), sh_d);
+    if (!pmode && !(tot > 0.0)) {  // residual is empty: draw from p
+        pmode = 1;
+        status |= SPEC_ROW_RESID_ZERO;
+        tot = 0.0;
+        for (int k0 = 0; k0 < C; k0 += kThreads) tot += block_sum(chunk_w(k0 + t), sh_d);
+    }
+    const RowPosUniforms u = row_pos_uniforms(seed, offset, (uint32_t)(row_base + b), (uint32_t)a);
+    const double tt = (double)u.smp * tot;
+    double carry = 0.0;
+    for (int k0 = 0; k0 < C; k0 += kThreads) {
+        const int k = k0 + t;
+        const double wk = chunk_w(k);
+        double btot;
+        const double incl = carry + block_incl_scan(wk, sh_d, &btot);
+        s_scan[t + 1] = incl;
+        if (t == 0) s_scan[0] = carry;
+        __syncthreads();
+        if (k < C && wk > 0.0) {
+            atomicMax(&s_lastpos, k);
+            if (incl > tt && s_scan[t] <= tt) {
+                s_cstar = k;  // unique: the scan is non-decreasing
+                s_tp = tt - s_scan[t];
+            }
+        }
+        __syncthreads();
+        if (s_cstar != 0x7FFFFFFF) break;
+        carry += btot;
+    }
+    int cstar = s_cstar;
+    double tp = s_tp;
+    if (cstar == 0x7FFFFFFF) {  // rounding left t at or past the total: last positive entry
+        cstar = s_lastpos;
+        tp = INFINITY;
+    }
+    __syncthreads();
+    if (t == 0) s_lastpos = -1;
+
+    // second level: scan the chosen chunk in index order
+    const int64_t start = (int64_t)cstar * kChunk + (int64_t)t * kTEPT;
+    float w[kTEPT];
     {
-        float z[kEPT];
-        load_contig<T, VEC>(zrow, V, start, z);
+        float z[kTEPT];
+        load_contig<T, VEC, kTEPT>(zrow, V, start, z);
         if (pmode) {
 #pragma unroll
-            for (int e = 0; e < kEPT; ++e) w[e] = p_weight(z[e], c, mcM);
+            for (int e = 0; e < kTEPT; ++e) w[e] = p_weight(z[e], c, mcM);
         } else {
-            float qq[kEPT];
-            load_q_contig<VEC>(qrow, V, start, qq);
+            float qq[kTEPT];
+            load_q_contig<VEC, kTEPT>(qrow, V, start, qq);
 #pragma unroll
-            for (int e = 0; e < kEPT; ++e) w[e] = r_weight(z[e], qq[e], c, mcM, invS);
+            for (int e = 0; e < kTEPT; ++e) w[e] = r_weight(z[e], qq[e], c, mcM, invS);
         }
     }
     double own = 0.0;
     int lastpos = -1;
 #pragma unroll
-    for (int e = 0; e < kEPT; ++e) {
+    for (int e = 0; e < kTEPT; ++e) {
         own += (double)w[e];
         if (w[e] > 0.f) lastpos = e;
     }
-    // exclusive scan of the per-thread sums: wave64 shuffle scan, then waves
-    {
-        const int lane = t & (kWave - 1);
-        double inc = own;
-#pragma unroll
-        for (int o = 1; o < kWave; o <<= 1) {
-            const double n = __shfl_up(inc, o, kWave);
-            if (lane >= o) inc += n;
-        }
-        const int wv = t / kWave;
-        if (lane == kWave - 1) sh_d[wv] = inc;
-        __syncthreads();
-        double base = 0.0;
-        for (int k = 0; k < wv; ++k) base += sh_d[k];
-        s_scan[t + 1] = base + inc;
-        if (t == 0) s_scan[0] = 0.0;
-    }
+    double ctot;
+    const double incl = block_incl_scan(own, sh_d, &ctot);
+    s_scan[t + 1] = incl;
+    if (t == 0) s_scan[0] = 0.0;
     __syncthreads();
     const double lo = s_scan[t], hi = s_scan[t + 1];
     if (lo <= tp && tp < hi) {
         double cum = lo;
         int found = -1;
 #pragma unroll
-        for (int e = 0; e < kEPT; ++e) {
+        for (int e = 0; e < kTEPT; ++e) {
             cum += (double)w[e];
             if (found < 0 && w[e] > 0.f && cum > tp) found = e;
         }
@@ -596,61 +728,70 @@ __global__ __launch_bounds__(kThreads) void k_finish(
     if (t == 0) {
         int tok = s_tok;
         if (tok == 0x7FFFFFFF) tok = s_lastpos;  // t' at or past the chunk total
-        for (int i = 0; i < a; ++i) out_tokens[b * (K + 1) + i] = tokens[b * K + i];
         out_tokens[b * (K + 1) + a] = tok;
-        for (int i = a + 1; i <= K; ++i) out_tokens[b * (K + 1) + i] = -1;
         out_accepted[b] = a;
         if (out_status) out_status[b] = status;
     }
+    for (int i = t; i <= K; i += kThreads)
+        if (i != a) out_tokens[b * (K + 1) + i] = (i < a) ? tokens[b * K + i] : -1;
 }
 
+// ---- greedy finish: one wave per row ---------------------------------------------------
 __global__ __launch_bounds__(kWave) void k_greedy_finish(
     const int32_t* __restrict__ tokens, const int32_t* __restrict__ lens, int K, int64_t V, int C,
     const ArgPart* __restrict__ part, int32_t* __restrict__ out_tokens,
     int32_t* __restrict__ out_accepted, float* __restrict__ out_p_draft,
     int32_t* __restrict__ out_status) {
     __shared__ int s_g[SPEC_MAX_DRAFT + 1];
-    __shared__ int s_match[SPEC_MAX_DRAFT + 1];
-    __shared__ int s_status;
+    __shared__ int s_status, s_a;
     const int64_t b = blockIdx.x;
     const int t = threadIdx.x;
     const int L = lens ? lens[b] : K;
     const bool len_ok = (L >= 0 && L <= K);
-    if (t == 0) s_status = len_ok ? 0 : SPEC_ROW_BAD_LEN;
+    if (t == 0) {
+        s_status = len_ok ? 0 : SPEC_ROW_BAD_LEN;
+        s_a = len_ok ? L : 0;
+    }
     __syncthreads();
     if (len_ok) {
-        for (int i = t; i <= L; i += kWave) {
+        // per position: lanes over chunks, butterfly (max value, lowest index)
+        for (int i = 0; i <= L; ++i) {
             const ArgPart* pp = part + ((b * (K + 1) + i) * C);
             float bv = -INFINITY;
             int bi = 0x7FFFFFFF, flag = 0;
-            for (int k = 0; k < C; ++k) {
+            for (int k = t; k < C; k += kWave) {
                 const ArgPart e = pp[k];
                 flag |= e.flag;
                 if (e.v > bv || (e.v == bv && e.idx < bi)) { bv = e.v; bi = e.idx; }
             }
-            if (bv == -INFINITY || bv == INFINITY) flag = 1;
-            int st = flag ? SPEC_ROW_NONFINITE : 0;
-            s_g[i] = bi;
-            int match = 0;
-            if (i < L) {
-                const int x = tokens[b * K + i];
-                if (x < 0 || (int64_t)x >= V) st |= SPEC_ROW_BAD_TOKEN;
-                match = (x == bi) ? 1 : 0;
+#pragma unroll
+            for (int o = kWave / 2; o > 0; o >>= 1) {
+                const float ov = __shfl_xor(bv, o, kWave);
+                const int oi = __shfl_xor(bi, o, kWave);
+                if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
             }
-            s_match[i] = match;
-            if (st) atomicOr(&s_status, st);
+            flag = wave_or(flag);
+            if (t == 0) {
+                s_g[i] = bi;
+                if (flag || bv == -INFINITY || bv == INFINITY) s_status |= SPEC_ROW_NONFINITE;
+            }
+        }
+        for (int i = t; i < L; i += kWave) {
+            const int x = tokens[b * K + i];
+            if (x < 0 || (int64_t)x >= V) atomicOr(&s_status, SPEC_ROW_BAD_TOKEN);
         }
     }
     __syncthreads();
+    if (len_ok)
+        for (int i = t; i < L; i += kWave)
+            if (tokens[b * K + i] != s_g[i]) atomicMin(&s_a, i);
+    __syncthreads();
     const int status = s_status;
     const bool invalid = (status & kInvalidMask) != 0;
-    int a = L;
-    if (!invalid)
-        for (int i = 0; i < L; ++i)
-            if (!s_match[i]) { a = i; break; }
+    const int a = s_a;
     if (out_p_draft)
         for (int i = t; i < K; i += kWave)
-            out_p_draft[b * K + i] = (!invalid && i < L) ? (float)s_match[i] : -1.f;
+            out_p_draft[b * K + i] = (!invalid && i < L) ? (tokens[b * K + i] == s_g[i] ? 1.f : 0.f) : -1.f;
     for (int i = t; i <= K; i += kWave) {
         int v = -1;
         if (!invalid) {
@@ -665,9 +806,9 @@ __global__ __launch_bounds__(kWave) void k_greedy_finish(
     }
 }
 
-// ---- host side ----------------------------------------------------------------
+// ---- host side ------------------------------------------------------------------------------
 struct AcceptWs {
-    size_t part_off, resid_off, count_off, total;
+    size_t part_off, resid_off, info_off, total;
 };
 
 AcceptWs accept_ws_layout(int64_t B, int K, int64_t V) {
@@ -675,8 +816,8 @@ AcceptWs accept_ws_layout(int64_t B, int K, int64_t V) {
     AcceptWs w;
     w.part_off = 0;
     w.resid_off = align_up((size_t)B * (K + 1) * C * sizeof(StatPart), 256);
-    w.count_off = w.resid_off + align_up((size_t)B * C * sizeof(double), 256);
-    w.total = w.count_off + align_up((size_t)B * sizeof(int32_t), 256);
+    w.info_off = w.resid_off + align_up((size_t)B * C * sizeof(double), 256);
+    w.total = w.info_off + align_up((size_t)B * sizeof(RowInfo), 256);
     return w;
 }
 
@@ -686,28 +827,34 @@ int launch_accept(const T* logits, const float* q, const int32_t* tokens, const 
                   uint64_t offset, int32_t* out_tokens, int32_t* out_accepted, float* out_p_draft,
                   int32_t* out_status, char* ws, const AcceptWs& lay, hipStream_t stream) {
     const int C = (int)((V + kChunk - 1) / kChunk);
-    const int64_t n1 = B * (K + 1) * C;
-    int32_t* counters = reinterpret_cast<int32_t*>(ws + lay.count_off);
+    const int64_t items = B * (K + 1) * C;
+    const unsigned g1 = (unsigned)(items < kStatsWaves ? items : kStatsWaves);
+    void* part = ws + lay.part_off;
     if (temperature == 0.f) {
-        ArgPart* part = reinterpret_cast<ArgPart*>(ws + lay.part_off);
-        hipLaunchKernelGGL((k_argmax<T, VEC>), dim3((unsigned)n1), dim3(kThreads), 0, stream,
-                           logits, lens, K, V, C, part);
+        hipLaunchKernelGGL((k_stats<T, VEC, true>), dim3(g1), dim3(kWave), 0, stream, logits, lens,
+                           B, K, V, C, 0.f, part);
         if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
         hipLaunchKernelGGL(k_greedy_finish, dim3((unsigned)B), dim3(kWave), 0, stream, tokens, lens,
-                           K, V, C, part, out_tokens, out_accepted, out_p_draft, out_status);
+                           K, V, C, static_cast<const ArgPart*>(part), out_tokens, out_accepted,
+                           out_p_draft, out_status);
         if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
         return SPEC_OK;
     }
     // c = log2(e) / T, rounded once to fp32
     const float c = (float)(1.4426950408889634074 / (double)temperature);
-    StatPart* part = reinterpret_cast<StatPart*>(ws + lay.part_off);
+    const StatPart* sp = static_cast<const StatPart*>(part);
     double* resid = reinterpret_cast<double*>(ws + lay.resid_off);
-    hipLaunchKernelGGL((k_stats<T, VEC>), dim3((unsigned)n1), dim3(kThreads), 0, stream, logits,
-                       lens, K, V, C, c, part, counters);
+    RowInfo* info = reinterpret_cast<RowInfo*>(ws + lay.info_off);
+    hipLaunchKernelGGL((k_stats<T, VEC, false>), dim3(g1), dim3(kWave), 0, stream, logits, lens,
+                       B, K, V, C, c, part);
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-    hipLaunchKernelGGL((k_finish<T, VEC>), dim3((unsigned)(B * C)), dim3(kThreads), 0, stream,
-                       logits, q, tokens, lens, K, V, C, c, row_base, seed, offset, part, resid,
-                       counters, out_tokens, out_accepted, out_p_draft, out_status);
+    hipLaunchKernelGGL((k_decide<T, VEC>), dim3((unsigned)(B * C)), dim3(kThreads), 0, stream,
+                       logits, q, tokens, lens, K, V, C, c, row_base, seed, offset, sp, resid, info,
+                       out_tokens, out_accepted, out_p_draft, out_status);
+    if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+    hipLaunchKernelGGL((k_sample<T, VEC>), dim3((unsigned)B), dim3(kThreads), 0, stream, logits, q,
+                       tokens, K, V, C, c, row_base, seed, offset, sp, resid, info, out_tokens,
+                       out_accepted, out_status);
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
     return SPEC_OK;
 }
@@ -740,8 +887,8 @@ extern "C" int spec_accept(const void* target_logits, int logits_dtype, const fl
     if (K > 0 && !draft_tokens) return SPEC_ERR_INVALID_ARG;
     if (temperature > 0.f && K > 0 && !draft_probs) return SPEC_ERR_INVALID_ARG;
     const int64_t C = (V + kChunk - 1) / kChunk;
-    // grid limits: launch 1 has B(K+1)C workgroups of 256 threads
-    if (B * (K + 1) * C > ((int64_t)1 << 24) || B * C > ((int64_t)1 << 24)) return SPEC_ERR_INVALID_ARG;
+    // grid limit: k_decide has B*C workgroups
+    if (B * C > ((int64_t)1 << 24) || B * (K + 1) * C > ((int64_t)1 << 40)) return SPEC_ERR_INVALID_ARG;
     const AcceptWs lay = accept_ws_layout(B, K, V);
     if (!workspace || workspace_bytes < lay.total || !aligned16(workspace)) return SPEC_ERR_WORKSPACE;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);

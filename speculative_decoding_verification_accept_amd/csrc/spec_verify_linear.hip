@@ -112,8 +112,10 @@ __global__ __launch_bounds__(kSkinnyWaves * kWave) void k_skinny(
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int64_t ntile = blockIdx.x;
-    const int64_t mtile = blockIdx.y;
+    // m-tiles sharing a column strip are adjacent in launch order, so their
+    // re-reads of that strip of W hit in cache
+    const int64_t mtile = blockIdx.x;
+    const int64_t ntile = blockIdx.y;
     const int split = blockIdx.z;
     const int64_t nb = ntile * kNT;
     const int64_t m0 = mtile * (16 * MT);
@@ -177,7 +179,7 @@ __global__ __launch_bounds__(kSkinnyWaves * kWave) void k_skinny(
     if (splits > 1) {
         // write this split's fp32 partial tile, then the last workgroup of the
         // tile sums all splits in order
-        const int64_t Mp = (int64_t)gridDim.y * 16 * MT;
+        const int64_t Mp = (int64_t)gridDim.x * 16 * MT;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
@@ -195,7 +197,7 @@ __global__ __launch_bounds__(kSkinnyWaves * kWave) void k_skinny(
         __threadfence();
         int last = 0;
         if (lane == 0) {
-            const int old = atomicAdd(&counters[mtile * gridDim.x + ntile], 1);
+            const int old = atomicAdd(&counters[ntile * gridDim.x + mtile], 1);
             last = (old == splits - 1);
         }
         last = __shfl(last, 0, kWave);
@@ -302,7 +304,7 @@ extern "C" int spec_verify_linear(const void* X, const void* W, void* Y, int y_d
     if (M == 0) return SPEC_OK;
     if (!X || !W || !Y || !aligned16(X) || !aligned16(W) || !aligned16(Y)) return SPEC_ERR_INVALID_ARG;
     const SkinnyPlan p = plan_skinny(M, N, Kd);
-    if (p.ntiles > 0x7FFFFFFF || p.mtiles > 65535) return SPEC_ERR_INVALID_ARG;
+    if (p.ntiles > 65535 || p.mtiles > 0x7FFFFFFF) return SPEC_ERR_INVALID_ARG;
     const size_t need = p.partial_bytes + p.counter_bytes;
     if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
         return SPEC_ERR_WORKSPACE;
@@ -316,7 +318,7 @@ extern "C" int spec_verify_linear(const void* X, const void* W, void* Y, int y_d
         hipLaunchKernelGGL(k_zero_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, counters, n);
         if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
     }
-    const dim3 grid((unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits);
+    const dim3 grid((unsigned)p.mtiles, (unsigned)p.ntiles, (unsigned)p.splits);
     const dim3 block(kSkinnyWaves * kWave);
     const size_t lds = 0;
     const uint16_t* x = static_cast<const uint16_t*>(X);

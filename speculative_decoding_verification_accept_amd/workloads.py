@@ -184,3 +184,33 @@ def linear_inputs(M: int, K: int, N: int, seed: int, device="cpu",
     X = (torch.randn(M, K, generator=g, device=device) * x_std).to(torch.bfloat16)
     W = (torch.randn(K, N, generator=g, device=device) * w_std).to(torch.bfloat16)
     return X, W
+
+
+# --- device-resident synthesis for the benchmark ------------------------------
+
+def draft_side_device(target_logits: torch.Tensor, K: int, draft_noise: float,
+                      temperature: float, gen: torch.Generator, ragged: bool = False):
+    """Draft side of a verify step synthesised on the GPU with torch ops: draft
+    logits = target logits (first K positions) + N(0, draft_noise^2), q =
+    softmax(draft / T) in fp32, x ~ q by torch.multinomial, and optional
+    ragged lengths L_b ~ U{1..K}.  target_logits is [B, K+1, V]."""
+    B, K1, V = target_logits.shape
+    dl = target_logits[:, :K, :].float()
+    dl = dl + draft_noise * torch.randn(dl.shape, generator=gen, device=dl.device)
+    q = torch.softmax(dl.double() / temperature, dim=-1).float().contiguous()
+    x = torch.multinomial(q.view(-1, V), 1, generator=gen).view(B, K).to(torch.int32)
+    if ragged:
+        L = torch.randint(1, K + 1, (B,), generator=gen, device=dl.device, dtype=torch.int32)
+    else:
+        L = torch.full((B,), K, dtype=torch.int32, device=dl.device)
+    return q, x.contiguous(), L
+
+
+def large_accept_device(seed: int, device, B: int = 64, K: int = 7, V: int = 128256):
+    """Device-resident inputs with the recipe of large_accept(): bf16 target
+    logits ~ N(0, 3^2), draft noise N(0, 1.5^2), T = 0.8, ragged L_b."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    z = (3.0 * torch.randn(B, K + 1, V, generator=g, device=device)).to(torch.bfloat16)
+    q, x, L = draft_side_device(z, K, 1.5, 0.8, g, ragged=True)
+    return z, q, x, L
