@@ -36,7 +36,10 @@
 
 #include <math.h>
 
+#include <atomic>
+
 namespace specv {
+int64_t resident_waves(const void* kernel);
 namespace {
 
 constexpr int kChunk = 4096;                 // vocabulary entries per chunk
@@ -46,7 +49,7 @@ constexpr int kTEPT = kChunk / kThreads;     // entries per thread there (16)
 constexpr int kWaves = kThreads / kWave;
 constexpr int kRegLens = 4;                  // lengths held in registers by k_stats
 constexpr int kCompactMaxB = kWave * kRegLens;
-constexpr int kStatsWaves = 4096;            // k_stats grid cap (single-wave workgroups)
+constexpr int kSampleRegs = 4;               // chunk weights held per thread by k_sample
 constexpr int kInvalidMask = SPEC_ROW_NONFINITE | SPEC_ROW_BAD_TOKEN | SPEC_ROW_BAD_LEN | SPEC_ROW_ZERO_Q;
 
 struct StatPart {  // stochastic partial of one (row, position, chunk)
@@ -64,9 +67,11 @@ struct RowInfo {  // k_decide -> k_sample
     int a;        // first rejection (or L_b)
     int status;   // SPEC_ROW_* bits
     int reject;   // a < L_b
-    int pad;
+    float M;      // max logit at position a
+    double S;     // p-frame normaliser at position a (frame fl(M c))
+    double pad;
 };
-static_assert(sizeof(StatPart) == 16 && sizeof(ArgPart) == 16 && sizeof(RowInfo) == 16, "layout");
+static_assert(sizeof(StatPart) == 16 && sizeof(ArgPart) == 16 && sizeof(RowInfo) == 32, "layout");
 
 typedef uint16_t bf16_t;
 
@@ -99,11 +104,16 @@ template <typename T, bool VEC, int NT, int EPT> struct Raw;
 template <int NT, int EPT> struct Raw<bf16_t, true, NT, EPT> {
     uint4 r[EPT / 8];
     __device__ __forceinline__ void load(const bf16_t* row, int64_t V, int64_t chunk0, int t) {
-        const uint4* p = reinterpret_cast<const uint4*>(row);
+        const uint4* p = reinterpret_cast<const uint4*>(row + chunk0) + t;
+        if (chunk0 + (int64_t)NT * EPT <= V) {  // whole chunk in range (uniform)
 #pragma unroll
-        for (int k = 0; k < EPT / 8; ++k) {
-            const int64_t vi = chunk0 / 8 + (int64_t)k * NT + t;
-            r[k] = (vi * 8 < V) ? p[vi] : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
+            for (int k = 0; k < EPT / 8; ++k) r[k] = p[k * NT];
+        } else {
+#pragma unroll
+            for (int k = 0; k < EPT / 8; ++k)
+                r[k] = (chunk0 + ((int64_t)k * NT + t) * 8 < V)
+                           ? p[k * NT]
+                           : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
         }
     }
     __device__ __forceinline__ void unpack(float (&v)[EPT]) const {
@@ -115,11 +125,16 @@ template <int NT, int EPT> struct Raw<bf16_t, true, NT, EPT> {
 template <int NT, int EPT> struct Raw<float, true, NT, EPT> {
     float4 r[EPT / 4];
     __device__ __forceinline__ void load(const float* row, int64_t V, int64_t chunk0, int t) {
-        const float4* p = reinterpret_cast<const float4*>(row);
+        const float4* p = reinterpret_cast<const float4*>(row + chunk0) + t;
+        if (chunk0 + (int64_t)NT * EPT <= V) {  // whole chunk in range (uniform)
 #pragma unroll
-        for (int k = 0; k < EPT / 4; ++k) {
-            const int64_t vi = chunk0 / 4 + (int64_t)k * NT + t;
-            r[k] = (vi * 4 < V) ? p[vi] : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            for (int k = 0; k < EPT / 4; ++k) r[k] = p[k * NT];
+        } else {
+#pragma unroll
+            for (int k = 0; k < EPT / 4; ++k)
+                r[k] = (chunk0 + ((int64_t)k * NT + t) * 4 < V)
+                           ? p[k * NT]
+                           : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         }
     }
     __device__ __forceinline__ void unpack(float (&v)[EPT]) const {
@@ -156,13 +171,14 @@ __device__ __forceinline__ void load_q_strided(const float* row, int64_t V, int6
                                                float (&v)[EPT]) {
     constexpr int W = Lay<T, VEC>::W;
     if constexpr (W > 1) {
-        const float4* p = reinterpret_cast<const float4*>(row);
+        const float4* p = reinterpret_cast<const float4*>(row + chunk0) + (int64_t)t * (W / 4);
+        const bool full = chunk0 + (int64_t)NT * EPT <= V;  // uniform
 #pragma unroll
         for (int k = 0; k < EPT / W; ++k) {
-            const int64_t vi = chunk0 / W + (int64_t)k * NT + t;
+            const bool ok = full || chunk0 + ((int64_t)k * NT + t) * W < V;
 #pragma unroll
             for (int h = 0; h < W / 4; ++h) {
-                const float4 f = (vi * W < V) ? p[vi * (W / 4) + h] : make_float4(0.f, 0.f, 0.f, 0.f);
+                const float4 f = ok ? p[(int64_t)k * NT * (W / 4) + h] : make_float4(0.f, 0.f, 0.f, 0.f);
                 v[k * W + 4 * h] = f.x; v[k * W + 4 * h + 1] = f.y;
                 v[k * W + 4 * h + 2] = f.z; v[k * W + 4 * h + 3] = f.w;
             }
@@ -403,21 +419,9 @@ __global__ __launch_bounds__(kWave) void k_stats(const T* __restrict__ logits,
     WorkList wl;
     wl.init(lens, B, K, C);
     const int64_t stride = gridDim.x;
-    int64_t w = blockIdx.x, rp = 0;
-    int ci = 0;
-    bool have = wl.next(w, stride, rp, ci);
-    Raw<T, VEC, kWave, kWEPT> cur;
-    if (have) cur.load(logits + rp * V, V, (int64_t)ci * kChunk, lane);
-    while (have) {
-        // issue the next item's loads before reducing this one
-        int64_t wn = w + stride, rpn = 0;
-        int cin = 0;
-        const bool haven = wl.next(wn, stride, rpn, cin);
-        Raw<T, VEC, kWave, kWEPT> nxt;
-        if (haven) nxt.load(logits + rpn * V, V, (int64_t)cin * kChunk, lane);
-
+    auto process = [&](const Raw<T, VEC, kWave, kWEPT>& raw, int64_t rp, int ci) {
         float v[kWEPT];
-        cur.unpack(v);
+        raw.unpack(v);
         const int64_t pidx = rp * C + ci;
         if constexpr (GREEDY) {
             const int64_t chunk0 = (int64_t)ci * kChunk;
@@ -473,11 +477,24 @@ __global__ __launch_bounds__(kWave) void k_stats(const T* __restrict__ logits,
             }
             if (lane == 0) static_cast<StatPart*>(part_out)[pidx] = StatPart{m, flag, s};
         }
-        cur = nxt;
-        w = wn;
-        rp = rpn;
-        ci = cin;
-        have = haven;
+    };
+    // two register buffers in ping-pong: the next item's loads are issued
+    // before the current item is reduced
+    Raw<T, VEC, kWave, kWEPT> bufA, bufB;
+    int64_t w = blockIdx.x, rpA = 0, rpB = 0;
+    int ciA = 0, ciB = 0;
+    bool haveA = wl.next(w, stride, rpA, ciA);
+    if (haveA) bufA.load(logits + rpA * V, V, (int64_t)ciA * kChunk, lane);
+    while (haveA) {
+        int64_t w2 = w + stride;
+        const bool haveB = wl.next(w2, stride, rpB, ciB);
+        if (haveB) bufB.load(logits + rpB * V, V, (int64_t)ciB * kChunk, lane);
+        process(bufA, rpA, ciA);
+        if (!haveB) break;
+        w = w2 + stride;
+        haveA = wl.next(w, stride, rpA, ciA);
+        if (haveA) bufA.load(logits + rpA * V, V, (int64_t)ciA * kChunk, lane);
+        process(bufB, rpB, ciB);
     }
 }
 
@@ -505,6 +522,7 @@ __global__ __launch_bounds__(kThreads) void k_decide(
     const int t = threadIdx.x;
     const int lane = t & (kWave - 1);
     const int wv = t / kWave;
+    const int x = (t < K) ? tokens[b * K + t] : 0;  // issued with the length load
     const int L = lens ? lens[b] : K;
     const bool len_ok = (L >= 0 && L <= K);
     if (t == 0) {
@@ -515,7 +533,6 @@ __global__ __launch_bounds__(kThreads) void k_decide(
 
     // gather z_i(x_i) and q_i(x_i) of every drafted position (one thread each)
     if (len_ok && t < L) {
-        const int x = tokens[b * K + t];
         int st = 0;
         float zx = 0.f, qx = 1.f;
         if (x < 0 || (int64_t)x >= V) {
@@ -574,12 +591,17 @@ __global__ __launch_bounds__(kThreads) void k_decide(
                 if (out_status) out_status[b] = status;
             }
         }
-        if (t == 0) info[b] = RowInfo{a, status, reject ? 1 : 0, 0};
+        if (t == 0) info[b] = RowInfo{a, status, reject ? 1 : 0, invalid ? 0.f : s_M[a], invalid ? 0.0 : s_S[a], 0.0};
     }
-    if (!reject) return;
+    if (invalid) return;
+    const float mcM = s_M[a] * c;
+    if (!reject) {
+        // the bonus draw uses the p-frame mass of each chunk at position a
+        if (t == 0) resid[b * C + ci] = chunk_p_mass(part[(b * (K + 1) + a) * C + ci], c, mcM);
+        return;
+    }
 
     // residual mass of this chunk at the rejected position
-    const float mcM = s_M[a] * c;
     const float invS = (float)(1.0 / s_S[a]);
     const T* zrow = logits + (b * (K + 1) + a) * V;
     const float* qrow = q + (b * K + a) * V;
@@ -611,43 +633,49 @@ __global__ __launch_bounds__(kThreads) void k_sample(
     int32_t* __restrict__ out_accepted, int32_t* __restrict__ out_status) {
     __shared__ double sh_d[kWaves];
     __shared__ double s_scan[kThreads + 1];
-    __shared__ float s_M;
-    __shared__ double s_S, s_tp;
+    __shared__ double s_tp;
     __shared__ int s_cstar, s_tok, s_lastpos;
 
     const int64_t b = blockIdx.x;
     const int t = threadIdx.x;
+    // the row's chunk weights and its decision record load together
+    double wreg[kSampleRegs];
+#pragma unroll
+    for (int j = 0; j < kSampleRegs; ++j) {
+        const int k = j * kThreads + t;
+        wreg[j] = (k < C) ? resid[b * C + k] : 0.0;
+    }
     const RowInfo ri = info[b];
     if (ri.status & kInvalidMask) return;  // k_decide wrote this row
     const int a = ri.a;
     int status = ri.status;
     const StatPart* pp = part + (b * (K + 1) + a) * C;
-    if (t < kWave) {
-        const PosStats ps = merge_position(pp, C, c);
-        if (t == 0) {
-            s_M = ps.M;
-            s_S = ps.S;
-            s_cstar = 0x7FFFFFFF;
-            s_tok = 0x7FFFFFFF;
-            s_lastpos = -1;
-        }
+    if (t == 0) {
+        s_cstar = 0x7FFFFFFF;
+        s_tok = 0x7FFFFFFF;
+        s_lastpos = -1;
     }
-    __syncthreads();
-    const float mcM = s_M * c;
-    const float invS = (float)(1.0 / s_S);
+    const float mcM = ri.M * c;
+    const float invS = (float)(1.0 / ri.S);
     const T* zrow = logits + (b * (K + 1) + a) * V;
     const float* qrow = ri.reject ? q + (b * K + a) * V : nullptr;
 
-    // first level: pick the chunk from the chunk masses
+    // first level: pick the chunk from the chunk masses (residual masses
+    // after a rejection, p-frame masses for the bonus token)
     int pmode = ri.reject ? 0 : 1;
     auto chunk_w = [&](int k) -> double {
         if (k >= C) return 0.0;
-        return pmode ? chunk_p_mass(pp[k], c, mcM) : resid[b * C + k];
+        const int j = k / kThreads;
+        if (pmode == 2 || j >= kSampleRegs) return (pmode == 2) ? chunk_p_mass(pp[k], c, mcM) : resid[b * C + k];
+        double r = wreg[0];
+#pragma unroll
+        for (int jj = 1; jj < kSampleRegs; ++jj) r = (j == jj) ? wreg[jj] : r;
+        return r;
     };
     double tot = 0.0;
     for (int k0 = 0; k0 < C; k0 += kThreads) tot += block_sum(chunk_w(k0 + t), sh_d);
     if (!pmode && !(tot > 0.0)) {  // residual is empty: draw from p
-        pmode = 1;
+        pmode = 2;
         status |= SPEC_ROW_RESID_ZERO;
         tot = 0.0;
         for (int k0 = 0; k0 < C; k0 += kThreads) tot += block_sum(chunk_w(k0 + t), sh_d);
@@ -828,7 +856,12 @@ int launch_accept(const T* logits, const float* q, const int32_t* tokens, const 
                   int32_t* out_status, char* ws, const AcceptWs& lay, hipStream_t stream) {
     const int C = (int)((V + kChunk - 1) / kChunk);
     const int64_t items = B * (K + 1) * C;
-    const unsigned g1 = (unsigned)(items < kStatsWaves ? items : kStatsWaves);
+    // k_stats is persistent: one generation of single-wave workgroups that
+    // fills the device, each walking several items
+    const int64_t cap = temperature == 0.f ? resident_waves((const void*)k_stats<T, VEC, true>)
+                                           : resident_waves((const void*)k_stats<T, VEC, false>);
+    if (cap <= 0) return SPEC_ERR_HIP;
+    const unsigned g1 = (unsigned)(items < cap ? items : cap);
     void* part = ws + lay.part_off;
     if (temperature == 0.f) {
         hipLaunchKernelGGL((k_stats<T, VEC, true>), dim3(g1), dim3(kWave), 0, stream, logits, lens,
@@ -862,6 +895,36 @@ int launch_accept(const T* logits, const float* q, const int32_t* tokens, const 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
+
+// Number of single-wave workgroups of `kernel` the current device holds at
+// once (compute units x resident workgroups per unit); a read-only property
+// of the device and the code object, cached per (kernel, device).
+int64_t resident_waves(const void* kernel) {
+    constexpr int kMaxDev = 64, kMaxKernels = 16;
+    static std::atomic<int64_t> cache[kMaxKernels][kMaxDev];
+    static std::atomic<const void*> keys[kMaxKernels];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    int slot = -1;
+    for (int i = 0; i < kMaxKernels; ++i) {
+        const void* k = keys[i].load();
+        if (k == kernel) { slot = i; break; }
+        if (k == nullptr) {
+            const void* expect = nullptr;
+            if (keys[i].compare_exchange_strong(expect, kernel) || expect == kernel) { slot = i; break; }
+        }
+    }
+    if (slot >= 0 && dev < kMaxDev) {
+        const int64_t v = cache[slot][dev].load();
+        if (v > 0) return v;
+    }
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWave, 0) != hipSuccess) return -1;
+    const int64_t v = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    if (slot >= 0 && dev < kMaxDev) cache[slot][dev].store(v);
+    return v;
+}
 }  // namespace specv
 
 using namespace specv;
