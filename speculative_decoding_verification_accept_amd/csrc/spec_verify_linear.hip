@@ -1,26 +1,34 @@
 // spec_verify_linear.hip -- verify linear layer Y[M, N] = X[M, K] W[K, N] on
-// gfx950 bf16 MFMA with fp32 accumulation.
+// gfx950 bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation.
 //
 // Method: page "New technical post reveals how speculative decoding
 // accelerates LLM inference without hurting accuracy" (agentnet.co.il),
 // sections "The formula behind the speedup" and "GEMM-M grows, a small batch
 // suffices": verifying D drafts turns every linear layer of the target from
-// M = B rows into M = B(1+D) rows; weights are read once per pass whatever M
-// is, so the layer stays memory-bound until M reaches the machine's
-// FLOP-per-byte ridge.
+// M = B rows into M = B(1+D) rows.  The weights are read once per pass
+// whatever M is, so the layer stays memory-bound until M reaches the
+// machine's FLOP-per-byte ridge (about 315 on MI355X), then turns
+// compute-bound.
 //
-// Kernel k_skinny: the product is computed transposed, Y^T = W^T X^T, on
-// v_mfma_f32_16x16x32_bf16.  W is stored input-major ([K, N], N contiguous)
-// while an MFMA operand wants 8 consecutive k per lane, so each lane loads an
-// 8(k) x 8(n) block of W with eight 16-byte row loads (16 lanes cover 256
-// contiguous bytes of a row: coalesced) and transposes it in registers with
-// v_perm_b32 into the A operands of eight MFMAs whose 16 output rows are the
-// strided columns n = nb + 8 i + c.  X (K contiguous) is the B operand as
-// stored.  W never goes through LDS; it streams from HBM exactly once per
-// m-tile.  Each wave covers 128 columns x 16*MT rows over a slice of K; the
-// four waves of a workgroup split K further and are reduced through LDS;
-// optional split-K across workgroups writes fp32 partials that the last
-// workgroup of a tile (integer atomic counter) sums in a fixed order.
+// W is stored input-major ([K, N], N contiguous) while an MFMA operand wants
+// 8 consecutive k per lane.  Both kernels load W with row-contiguous 16- or
+// 8-byte loads and transpose small blocks in registers with v_perm_b32; X
+// (K contiguous) is used as stored.  The MFMA computes D = A B with A an X
+// fragment (16 rows m x 32 k) and B a W fragment (32 k x 16 columns n).
+//
+//  k_strip (M <= 32, memory-bound): one 512-thread workgroup per 64-column
+//    strip of W, all M rows, the full K.  Each of its 8 waves takes a slice
+//    of K, keeps 4 k-steps of W loads in flight, transposes each lane's 8x4
+//    block straight into MFMA operands (no LDS for W), and the waves' partial
+//    tiles are summed through LDS in a fixed order.  W streams from HBM
+//    exactly once.
+//  k_tile (M > 32, v_mfma_f32_32x32x16_bf16): a workgroup computes a BM x BN
+//    tile.  Each K-stage of W
+//    is transposed in registers on its way into LDS ([n][k], k contiguous),
+//    X is staged as stored, and every wave reads its fragments from LDS, so
+//    one HBM read of W serves all BM rows; the next stage's global loads are
+//    in flight while the MFMAs of the current one run.  Split-K writes fp32
+//    partials that k_reduce sums in a fixed order (no atomics).
 #include "spec_verify.h"
 #include "device_common.hpp"
 
@@ -30,18 +38,25 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kNT = 128;  // columns per wave tile
-constexpr int kKS = 32;   // k per MFMA step
-constexpr int kSkinnyWaves = 4;
+constexpr int kKS = 32;  // k per MFMA
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ f32x4_t mfma(uint4 a, uint4 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+// 32x32x16: A lane l = rows l % 32, k 8 (l / 32) .. +7; B likewise by column;
+// D register j of lane l = row 8 (j / 4) + 4 (l / 32) + j % 4, column l % 32.
+__device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
 
-// Column c (0..7) of an 8x8 bf16 block held as 8 row vectors r[0..7]
-// (row = k, 8 bf16 columns per uint4) -> 8 k values of that column.
-template <int C>
-__device__ __forceinline__ uint4 column_of(const uint4 (&r)[8]) {
+// 8 consecutive k of column C from 8 rows (row r = k) whose dword D holds
+// columns 2D (low half) and 2D+1 (high half).
+template <int C, typename Row>
+__device__ __forceinline__ uint4 column_of(const Row (&r)[8]) {
     constexpr uint32_t sel = (C & 1) ? 0x07060302u : 0x05040100u;
-    auto dw = [](const uint4& v) -> uint32_t {
+    auto dw = [](const Row& v) -> uint32_t {
         if constexpr (C / 2 == 0) return v.x;
         else if constexpr (C / 2 == 1) return v.y;
         else if constexpr (C / 2 == 2) return v.z;
@@ -55,232 +70,454 @@ __device__ __forceinline__ uint4 column_of(const uint4 (&r)[8]) {
     return o;
 }
 
+__device__ __forceinline__ void store_out(void* Y, int y_bf16, int64_t idx, f32x4_t v) {
+    if (y_bf16) {
+        uint2 o;
+        o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+        o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + idx) = o;
+    } else {
+        *reinterpret_cast<f32x4_t*>(static_cast<float*>(Y) + idx) = v;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_strip
+// Lane l of a wave: li = l % 16 owns columns n0 + 4 li .. +3, kg = l / 16 the
+// k rows 8 kg .. 8 kg + 7 of each 32-k step.  MFMA c (c = 0..3) takes as B
+// the column n0 + 4 j + c of lane j's block, so accumulator (c, mt) of lane l
+// holds Y[m0 + 16 mt + 4 (l / 16) + r][n0 + 4 (l % 16) + c], r = 0..3.
+constexpr int kStripN = 64;
+constexpr int kStripWaves = 8;
+constexpr int kStripDepth = 4;  // k-steps of W loads in flight per wave
+
 template <int MT>
-struct SkinnyAcc {
-    f32x4_t a[8][MT];
+struct StripStage {
+    uint2 w[8];
+    uint4 x[MT];
 };
 
 template <int MT>
-__device__ __forceinline__ void skinny_load(const uint16_t* __restrict__ X,
-                                            const uint16_t* __restrict__ W, int64_t M, int64_t N,
-                                            int64_t K, int64_t m0, int64_t nb, int64_t k0, int lane,
-                                            uint4 (&w)[8], uint4 (&x)[MT]) {
-    const int kg = lane >> 4;      // k group of 8
-    const int li = lane & 15;
-    const int64_t ncol = nb + 8 * li;
-    const bool nok = ncol < N;
+__device__ __forceinline__ void strip_load(const uint16_t* __restrict__ X,
+                                           const uint16_t* __restrict__ W, int64_t M, int64_t N,
+                                           int64_t K, int64_t m0, int64_t n0, int64_t s, int lane,
+                                           StripStage<MT>& st) {
+    const int kg = lane >> 4, li = lane & 15;
+    const int64_t ncol = n0 + 4 * li;
+    const int64_t k8 = s * kKS + 8 * kg;  // first of this lane's 8 k (all < K or none, K % 8 == 0)
+    const bool wok = ncol < N && k8 < K;
+    const uint16_t* wp = W + k8 * N + ncol;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const int64_t k = k0 + 8 * kg + r;
-        w[r] = (nok && k < K) ? *reinterpret_cast<const uint4*>(W + k * N + ncol)
-                              : make_uint4(0u, 0u, 0u, 0u);
-    }
-    const int64_t kx = k0 + 8 * kg;
+    for (int r = 0; r < 8; ++r)
+        st.w[r] = wok ? *reinterpret_cast<const uint2*>(wp + (int64_t)r * N) : make_uint2(0u, 0u);
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         const int64_t m = m0 + 16 * mt + li;
-        x[mt] = (m < M && kx < K) ? *reinterpret_cast<const uint4*>(X + m * K + kx)
-                                  : make_uint4(0u, 0u, 0u, 0u);
+        st.x[mt] = (m < M && k8 < K) ? *reinterpret_cast<const uint4*>(X + m * K + k8)
+                                     : make_uint4(0u, 0u, 0u, 0u);
     }
 }
 
 template <int MT>
-__device__ __forceinline__ void skinny_mma(const uint4 (&w)[8], const uint4 (&x)[MT],
-                                           SkinnyAcc<MT>& acc) {
-    uint4 col[8];
-    col[0] = column_of<0>(w); col[1] = column_of<1>(w);
-    col[2] = column_of<2>(w); col[3] = column_of<3>(w);
-    col[4] = column_of<4>(w); col[5] = column_of<5>(w);
-    col[6] = column_of<6>(w); col[7] = column_of<7>(w);
+__device__ __forceinline__ void strip_mma(const StripStage<MT>& st, f32x4_t (&acc)[4][MT]) {
+    const uint4 c0 = column_of<0>(st.w), c1 = column_of<1>(st.w);
+    const uint4 c2 = column_of<2>(st.w), c3 = column_of<3>(st.w);
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            acc.a[c][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(col[c]),
-                                                                   as_bf16x8(x[mt]),
-                                                                   acc.a[c][mt], 0, 0, 0);
+    for (int mt = 0; mt < MT; ++mt) {
+        acc[0][mt] = mfma(st.x[mt], c0, acc[0][mt]);
+        acc[1][mt] = mfma(st.x[mt], c1, acc[1][mt]);
+        acc[2][mt] = mfma(st.x[mt], c2, acc[2][mt]);
+        acc[3][mt] = mfma(st.x[mt], c3, acc[3][mt]);
+    }
 }
 
-// Output element of accumulator (c, mt, r) at lane l:
-//   n = nb + 8 * (4 * (l / 16) + r) + c,  m = m0 + 16 * mt + l % 16.
-// For fixed (mt, r) the eight c values are 8 consecutive columns.
 template <int MT>
-__global__ __launch_bounds__(kSkinnyWaves * kWave) void k_skinny(
+__global__ __launch_bounds__(kStripWaves * kWave) void k_strip(
     const uint16_t* __restrict__ X, const uint16_t* __restrict__ W, void* __restrict__ Y,
-    int y_bf16, int64_t M, int64_t N, int64_t K, int splits, float* __restrict__ partial,
-    int32_t* __restrict__ counters) {
+    int y_bf16, int64_t M, int64_t N, int64_t K) {
+    __shared__ f32x4_t red[(kStripWaves - 1) * kWave * 4];
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    // m-tiles sharing a column strip are adjacent in launch order, so their
-    // re-reads of that strip of W hit in cache
-    const int64_t mtile = blockIdx.x;
-    const int64_t ntile = blockIdx.y;
-    const int split = blockIdx.z;
-    const int64_t nb = ntile * kNT;
-    const int64_t m0 = mtile * (16 * MT);
-
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int64_t m0 = (int64_t)blockIdx.x * 16 * MT;   // m-tiles of a strip are adjacent
+    const int64_t n0 = (int64_t)blockIdx.y * kStripN;
     const int64_t nsteps = (K + kKS - 1) / kKS;
-    const int64_t g = (int64_t)split * kSkinnyWaves + wave;
-    const int64_t gtot = (int64_t)splits * kSkinnyWaves;
-    const int64_t s0 = g * nsteps / gtot, s1 = (g + 1) * nsteps / gtot;
+    const int64_t s0 = wave * nsteps / kStripWaves, s1 = (wave + 1) * nsteps / kStripWaves;
 
-    SkinnyAcc<MT> acc;
+    f32x4_t acc[4][MT];
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < 4; ++c)
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) acc.a[c][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int mt = 0; mt < MT; ++mt) acc[c][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    if (s0 < s1) {
-        uint4 w0[8], x0[MT];
-        skinny_load<MT>(X, W, M, N, K, m0, nb, s0 * kKS, lane, w0, x0);
-        for (int64_t s = s0; s < s1; ++s) {
-            uint4 w1[8], x1[MT];
-            const bool more = s + 1 < s1;
-            if (more) skinny_load<MT>(X, W, M, N, K, m0, nb, (s + 1) * kKS, lane, w1, x1);
-            skinny_mma<MT>(w0, x0, acc);
-            if (more) {
+    StripStage<MT> buf[kStripDepth];
 #pragma unroll
-                for (int r = 0; r < 8; ++r) w0[r] = w1[r];
+    for (int d = 0; d < kStripDepth; ++d)
+        if (s0 + d < s1) strip_load<MT>(X, W, M, N, K, m0, n0, s0 + d, lane, buf[d]);
+    for (int64_t base = s0; base < s1; base += kStripDepth) {
 #pragma unroll
-                for (int mt = 0; mt < MT; ++mt) x0[mt] = x1[mt];
+        for (int d = 0; d < kStripDepth; ++d) {
+            const int64_t s = base + d;
+            if (s < s1) {
+                strip_mma<MT>(buf[d], acc);
+                if (s + kStripDepth < s1)
+                    strip_load<MT>(X, W, M, N, K, m0, n0, s + kStripDepth, lane, buf[d]);
             }
         }
     }
 
-    // reduce the four waves' k-slices through LDS, one 16-row block at a
-    // time (fixed order: wave 0 + 1 + 2 + 3)
-    __shared__ float lds[(kSkinnyWaves - 1) * 64 * 32];
+    // fixed-order sum of the 8 waves' k-slices, one 16-row block at a time
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
         if (wave > 0) {
-            float* dst = lds + ((wave - 1) * 64 + lane) * 32;
 #pragma unroll
-            for (int c = 0; c < 8; ++c)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dst[c * 4 + r] = acc.a[c][mt][r];
+            for (int c = 0; c < 4; ++c) red[((wave - 1) * kWave + lane) * 4 + c] = acc[c][mt];
         }
         __syncthreads();
         if (wave == 0) {
-            for (int wv = 1; wv < kSkinnyWaves; ++wv) {
-                const float* src = lds + ((wv - 1) * 64 + lane) * 32;
+            for (int wv = 1; wv < kStripWaves; ++wv)
 #pragma unroll
-                for (int c = 0; c < 8; ++c)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc.a[c][mt][r] += src[c * 4 + r];
-            }
+                for (int c = 0; c < 4; ++c) acc[c][mt] += red[((wv - 1) * kWave + lane) * 4 + c];
         }
         __syncthreads();
     }
     if (wave != 0) return;
-
-    const int li = lane & 15;
-    const int kg = lane >> 4;
-    if (splits > 1) {
-        // write this split's fp32 partial tile, then the last workgroup of the
-        // tile sums all splits in order
-        const int64_t Mp = (int64_t)gridDim.x * 16 * MT;
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int64_t m = m0 + 16 * mt + li;
-                const int64_t n = nb + 8 * (4 * kg + r);
-                if (m < M && n < N) {
-                    float* p = partial + ((int64_t)split * Mp + m) * N + n;
-                    const f32x4_t lo = {acc.a[0][mt][r], acc.a[1][mt][r], acc.a[2][mt][r], acc.a[3][mt][r]};
-                    const f32x4_t hi = {acc.a[4][mt][r], acc.a[5][mt][r], acc.a[6][mt][r], acc.a[7][mt][r]};
-                    __builtin_nontemporal_store(lo, reinterpret_cast<f32x4_t*>(p));
-                    __builtin_nontemporal_store(hi, reinterpret_cast<f32x4_t*>(p + 4));
-                }
-            }
-        __threadfence();
-        int last = 0;
-        if (lane == 0) {
-            const int old = atomicAdd(&counters[ntile * gridDim.x + mtile], 1);
-            last = (old == splits - 1);
-        }
-        last = __shfl(last, 0, kWave);
-        if (!last) return;
-        __threadfence();
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-#pragma unroll
-                for (int c = 0; c < 8; ++c) acc.a[c][mt][r] = 0.f;
-        for (int sp = 0; sp < splits; ++sp) {
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int64_t m = m0 + 16 * mt + li;
-                    const int64_t n = nb + 8 * (4 * kg + r);
-                    if (m < M && n < N) {
-                        const float* p = partial + ((int64_t)sp * Mp + m) * N + n;
-                        const f32x4_t lo = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
-                        const f32x4_t hi = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p + 4));
-                        acc.a[0][mt][r] += lo[0]; acc.a[1][mt][r] += lo[1];
-                        acc.a[2][mt][r] += lo[2]; acc.a[3][mt][r] += lo[3];
-                        acc.a[4][mt][r] += hi[0]; acc.a[5][mt][r] += hi[1];
-                        acc.a[6][mt][r] += hi[2]; acc.a[7][mt][r] += hi[3];
-                    }
-                }
-        }
-    }
-
+    const int li = lane & 15, kg = lane >> 4;
+    const int64_t n = n0 + 4 * li;
+    if (n >= N) return;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t m = m0 + 16 * mt + li;
-            const int64_t n = nb + 8 * (4 * kg + r);
-            if (m >= M || n >= N) continue;
-            if (y_bf16) {
-                uint4 o;
-                o.x = (uint32_t)f32_to_bf16(acc.a[0][mt][r]) | ((uint32_t)f32_to_bf16(acc.a[1][mt][r]) << 16);
-                o.y = (uint32_t)f32_to_bf16(acc.a[2][mt][r]) | ((uint32_t)f32_to_bf16(acc.a[3][mt][r]) << 16);
-                o.z = (uint32_t)f32_to_bf16(acc.a[4][mt][r]) | ((uint32_t)f32_to_bf16(acc.a[5][mt][r]) << 16);
-                o.w = (uint32_t)f32_to_bf16(acc.a[6][mt][r]) | ((uint32_t)f32_to_bf16(acc.a[7][mt][r]) << 16);
-                *reinterpret_cast<uint4*>(static_cast<uint16_t*>(Y) + m * N + n) = o;
-            } else {
-                float* p = static_cast<float*>(Y) + m * N + n;
-                *reinterpret_cast<float4*>(p) = make_float4(acc.a[0][mt][r], acc.a[1][mt][r], acc.a[2][mt][r], acc.a[3][mt][r]);
-                *reinterpret_cast<float4*>(p + 4) = make_float4(acc.a[4][mt][r], acc.a[5][mt][r], acc.a[6][mt][r], acc.a[7][mt][r]);
+            const int64_t m = m0 + 16 * mt + 4 * kg + r;
+            if (m < M)
+                store_out(Y, y_bf16, m * N + n,
+                          f32x4_t{acc[0][mt][r], acc[1][mt][r], acc[2][mt][r], acc[3][mt][r]});
+        }
+}
+
+// ---------------------------------------------------------------------------
+// k_tile (v_mfma_f32_32x32x16_bf16: the 16x16x32 shape issues at half its
+// rate on gfx950)
+// LDS tiles (bf16, rows padded by 8 elements against bank conflicts):
+//   Ws[n][k]  BN x (BK + 8): W transposed, 8 consecutive k per 16 bytes
+//   Xs[m][k]  BM x (BK + 8)
+// Wave (wm, wn) computes rows wm*WM .. +WM and columns wn*WN .. +WN of the
+// tile: FM = WM/32 X fragments and FN = WN/32 W fragments per 16-k step.
+// Register j of accumulator (fm, fn) of lane l holds
+//   Y[m = 32 fm + 8 (j / 4) + 4 (l / 32) + j % 4][n = 32 fn + l % 32].
+template <int BM_, int BN_, int BK_, int WM_, int WN_>
+struct TileCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr int NWM = BM / WM, NWN = BN / WN;
+    static constexpr int NT = NWM * NWN * kWave;
+    static constexpr int FM = WM / 32, FN = WN / 32;  // 32x32 output blocks per wave
+    static constexpr int LDK = BK + 8;
+    static constexpr int WBLK_TOTAL = (BK / 8) * (BN / 8);       // 8x8 blocks of W per stage
+    static constexpr int WBLK = (WBLK_TOTAL + NT - 1) / NT;      // per thread
+    static constexpr int XV_TOTAL = BM * BK / 8;                 // 16-byte vectors of X per stage
+    static constexpr int XV = (XV_TOTAL + NT - 1) / NT;
+    static constexpr size_t LDS = (size_t)(BN + BM) * LDK * 2;
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile");
+    static_assert(BK == 64, "the LDS swizzle assumes 8 groups of 8 k per row");
+    static_assert(BN % 128 == 0, "the LDS swizzle assumes 16 column blocks per k-block row");
+};
+
+// Physical 16-byte k-group of logical group G in W row n of the LDS tile:
+// G ^ ((n >> 4) & 7).  With the 72-element row pitch (36 banks), both the
+// transposed stores (16 lanes: rows 8 nb + c, nb = 0..15) and the MFMA
+// fragment reads (16 lanes: 16 consecutive rows) then touch 16 disjoint
+// 4-bank ranges.
+__device__ __forceinline__ int w_group(int G, int n_over_16) { return G ^ (n_over_16 & 7); }
+
+template <typename Cfg>
+struct TileRegs {
+    uint4 w[Cfg::WBLK][8];
+    uint4 x[Cfg::XV];
+};
+
+// Loop-invariant per-thread addressing of k_tile.  Global loads are buffer
+// loads: the per-lane byte offset is fixed for the whole K loop and a stage
+// only moves the scalar offset; a lane whose element lies outside the matrix
+// gets an offset past the buffer's end, which the hardware reads as zero.
+template <typename Cfg>
+struct TileAddr {
+    __amdgpu_buffer_rsrc_t wr, xr;
+    uint32_t wv[Cfg::WBLK];   // W block (8 rows) byte offset within a stage, row 0
+    uint32_t xv[Cfg::XV];     // X vector byte offset within a stage
+    uint32_t wlds[Cfg::WBLK]; // LDS byte offset of the block's column 0 (within the W tile)
+    uint32_t xlds[Cfg::XV];   // LDS byte offset of the X vector (within the X tile)
+    uint32_t row_bytes;       // N * 2
+    uint32_t x_kok[Cfg::XV];  // k offset (elements) of the X vector within a stage
+};
+
+constexpr uint32_t kOOB = 0x80000000u;  // offset past any buffer below 2 GiB
+
+template <typename Cfg>
+__device__ __forceinline__ void tile_addr(const uint16_t* X, const uint16_t* W, int64_t M, int64_t N,
+                                          int64_t K, int64_t m0, int64_t n0, int tid,
+                                          TileAddr<Cfg>& A) {
+    const uint64_t wbytes = (uint64_t)K * N * 2, xbytes = (uint64_t)M * K * 2;
+    A.wr = __builtin_amdgcn_make_buffer_rsrc((void*)W, (short)0, (int)(wbytes < kOOB ? wbytes : kOOB - 1), 0x00020000);
+    A.xr = __builtin_amdgcn_make_buffer_rsrc((void*)X, (short)0, (int)(xbytes < kOOB ? xbytes : kOOB - 1), 0x00020000);
+    A.row_bytes = (uint32_t)(N * 2);
+#pragma unroll
+    for (int j = 0; j < Cfg::WBLK; ++j) {
+        const int q = tid + j * Cfg::NT;
+        const int kb = q / (Cfg::BN / 8), nb = q % (Cfg::BN / 8);
+        const int64_t n = n0 + 8 * nb;
+        A.wv[j] = (q < Cfg::WBLK_TOTAL && n < N) ? (uint32_t)(((int64_t)8 * kb * N + n) * 2) : kOOB;
+        // rows 8 nb .. 8 nb + 7 of the transposed tile share the swizzle (n >> 4) = nb >> 1
+        A.wlds[j] = (uint32_t)((8 * nb) * Cfg::LDK * 2 + 16 * w_group(kb, nb >> 1));
+    }
+#pragma unroll
+    for (int j = 0; j < Cfg::XV; ++j) {
+        const int v = tid + j * Cfg::NT;
+        const int mm = v / (Cfg::BK / 8), kv = v % (Cfg::BK / 8);
+        const int64_t m = m0 + mm;
+        A.xv[j] = (v < Cfg::XV_TOTAL && m < M) ? (uint32_t)((m * K + 8 * kv) * 2) : kOOB;
+        A.xlds[j] = (uint32_t)(mm * Cfg::LDK * 2 + 16 * kv);
+        A.x_kok[j] = 8 * kv;
+    }
+}
+
+__device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// Global loads of the stage starting at k0.  W rows past K lie past the end
+// of W (zero); X vectors past K within a row are masked only when the stage
+// crosses K.
+template <typename Cfg>
+__device__ __forceinline__ void tile_load(const TileAddr<Cfg>& A, int64_t K, int64_t k0,
+                                          TileRegs<Cfg>& R) {
+    const uint32_t wst = (uint32_t)(k0 * A.row_bytes);
+#pragma unroll
+    for (int j = 0; j < Cfg::WBLK; ++j)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) R.w[j][r] = bload(A.wr, A.wv[j], wst + r * A.row_bytes);
+    const bool tail = k0 + Cfg::BK > K;
+#pragma unroll
+    for (int j = 0; j < Cfg::XV; ++j) {
+        const uint32_t vo = (tail && k0 + A.x_kok[j] >= K) ? kOOB : A.xv[j];
+        R.x[j] = bload(A.xr, vo, (uint32_t)(k0 * 2));
+    }
+}
+
+template <typename Cfg>
+__device__ __forceinline__ void tile_store(const TileRegs<Cfg>& R, const TileAddr<Cfg>& A,
+                                           char* Ws, char* Xs, int tid) {
+#pragma unroll
+    for (int j = 0; j < Cfg::WBLK; ++j) {
+        if (Cfg::WBLK_TOTAL % Cfg::NT != 0 && tid + j * Cfg::NT >= Cfg::WBLK_TOTAL) continue;
+        char* base = Ws + A.wlds[j];
+        *reinterpret_cast<uint4*>(base + 0 * Cfg::LDK * 2) = column_of<0>(R.w[j]);
+        *reinterpret_cast<uint4*>(base + 1 * Cfg::LDK * 2) = column_of<1>(R.w[j]);
+        *reinterpret_cast<uint4*>(base + 2 * Cfg::LDK * 2) = column_of<2>(R.w[j]);
+        *reinterpret_cast<uint4*>(base + 3 * Cfg::LDK * 2) = column_of<3>(R.w[j]);
+        *reinterpret_cast<uint4*>(base + 4 * Cfg::LDK * 2) = column_of<4>(R.w[j]);
+        *reinterpret_cast<uint4*>(base + 5 * Cfg::LDK * 2) = column_of<5>(R.w[j]);
+        *reinterpret_cast<uint4*>(base + 6 * Cfg::LDK * 2) = column_of<6>(R.w[j]);
+        *reinterpret_cast<uint4*>(base + 7 * Cfg::LDK * 2) = column_of<7>(R.w[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < Cfg::XV; ++j) {
+        if (Cfg::XV_TOTAL % Cfg::NT != 0 && tid + j * Cfg::NT >= Cfg::XV_TOTAL) continue;
+        *reinterpret_cast<uint4*>(Xs + A.xlds[j]) = R.x[j];
+    }
+}
+
+// MFMAs of one stage.  abase: byte offset of this lane's first X fragment
+// row; brow[fn]: byte offset of this lane's W row of fragment fn; bsw[fn]: its
+// swizzle (n >> 4) & 7.
+template <typename Cfg>
+__device__ __forceinline__ void tile_compute(const char* Ws, const char* Xs, uint32_t abase,
+                                             const uint32_t (&brow)[Cfg::FN], const int (&bsw)[Cfg::FN],
+                                             int g, f32x16_t (&acc)[Cfg::FM][Cfg::FN]) {
+#pragma unroll
+    for (int k16 = 0; k16 < Cfg::BK / 16; ++k16) {
+        uint4 a[Cfg::FM], b[Cfg::FN];
+#pragma unroll
+        for (int fm = 0; fm < Cfg::FM; ++fm)
+            a[fm] = *reinterpret_cast<const uint4*>(Xs + abase + fm * 32 * Cfg::LDK * 2 + k16 * 32);
+#pragma unroll
+        for (int fn = 0; fn < Cfg::FN; ++fn)
+            b[fn] = *reinterpret_cast<const uint4*>(Ws + brow[fn] + 16 * ((2 * k16 + g) ^ bsw[fn]));
+#pragma unroll
+        for (int fm = 0; fm < Cfg::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < Cfg::FN; ++fn) acc[fm][fn] = mfma32(a[fm], b[fn], acc[fm][fn]);
+    }
+}
+
+// D register slots of global loads in flight and two LDS buffers.  Iteration
+// st: issue the global loads of stage st + D, multiply stage st out of one
+// LDS buffer, write stage st + 1 into the other, one barrier.
+template <typename Cfg, int D>
+__global__ __launch_bounds__(Cfg::NT) void k_tile(const uint16_t* __restrict__ X,
+                                                  const uint16_t* __restrict__ W,
+                                                  void* __restrict__ Y, int y_bf16, int64_t M,
+                                                  int64_t N, int64_t K, int splits,
+                                                  float* __restrict__ partial) {
+    static_assert(D % 2 == 0, "the LDS buffer of a stage is fixed by its slot");
+    extern __shared__ __align__(16) char lds[];
+    constexpr int STAGE = (Cfg::BN + Cfg::BM) * Cfg::LDK * 2;  // bytes
+    constexpr int XOFF = Cfg::BN * Cfg::LDK * 2;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int wm = wave / Cfg::NWN, wn = wave % Cfg::NWN;
+    const int64_t m0 = (int64_t)blockIdx.x * Cfg::BM;  // m-tiles of a column strip are adjacent
+    const int64_t n0 = (int64_t)blockIdx.y * Cfg::BN;
+    const int split = blockIdx.z;
+    const int64_t nst = (K + Cfg::BK - 1) / Cfg::BK;
+    const int64_t st0 = split * nst / splits, st1 = (split + 1) * nst / splits;
+
+    TileAddr<Cfg> A;
+    tile_addr<Cfg>(X, W, M, N, K, m0, n0, tid, A);
+    const int l32 = lane & 31, g = lane >> 5;
+    const uint32_t abase = (uint32_t)((wm * Cfg::WM + l32) * Cfg::LDK * 2 + 16 * g);
+    uint32_t brow[Cfg::FN];
+    int bsw[Cfg::FN];
+#pragma unroll
+    for (int fn = 0; fn < Cfg::FN; ++fn) {
+        const int n = wn * Cfg::WN + 32 * fn + l32;
+        brow[fn] = (uint32_t)(n * Cfg::LDK * 2);
+        bsw[fn] = (n >> 4) & 7;
+    }
+
+    f32x16_t acc[Cfg::FM][Cfg::FN];
+#pragma unroll
+    for (int a = 0; a < Cfg::FM; ++a)
+#pragma unroll
+        for (int b = 0; b < Cfg::FN; ++b)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.f;
+
+    TileRegs<Cfg> R[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (st0 + d < st1) tile_load<Cfg>(A, K, (st0 + d) * Cfg::BK, R[d]);
+    if (st0 < st1) tile_store<Cfg>(R[0], A, lds, lds + XOFF, tid);
+    __syncthreads();
+    for (int64_t base = st0; base < st1; base += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            const int64_t st = base + d;
+            if (st < st1) {
+                // slot d held stage st, already in LDS: refill it with stage st + D
+                if (st + D < st1) tile_load<Cfg>(A, K, (st + D) * Cfg::BK, R[d]);
+                const char* cur = lds + (d % 2) * STAGE;
+                tile_compute<Cfg>(cur, cur + XOFF, abase, brow, bsw, g, acc);
+                if (st + 1 < st1) {
+                    char* nxt = lds + ((d + 1) % 2) * STAGE;
+                    tile_store<Cfg>(R[(d + 1) % D], A, nxt, nxt + XOFF, tid);
+                }
+                __syncthreads();
+            }
+        }
+    }
+
+    float* dstp = splits > 1 ? partial + (int64_t)split * M * N : nullptr;
+#pragma unroll
+    for (int fm = 0; fm < Cfg::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < Cfg::FN; ++fn) {
+            const int64_t n = n0 + wn * Cfg::WN + 32 * fn + l32;
+            if (n >= N) continue;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int64_t m = m0 + wm * Cfg::WM + 32 * fm + 8 * (j / 4) + 4 * g + (j % 4);
+                if (m >= M) continue;
+                const float v = acc[fm][fn][j];
+                if (dstp) dstp[m * N + n] = v;
+                else if (y_bf16) static_cast<uint16_t*>(Y)[m * N + n] = f32_to_bf16(v);
+                else static_cast<float*>(Y)[m * N + n] = v;
             }
         }
 }
 
-__global__ void k_zero_i32(int32_t* __restrict__ p, int64_t n) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) p[i] = 0;
+// Sum of split-K partials in split order.
+__global__ void k_reduce(const float* __restrict__ partial, void* __restrict__ Y, int y_bf16,
+                         int64_t MN, int splits) {
+    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (i >= MN) return;  // MN % 4 == 0 (N % 8 == 0)
+    f32x4_t s = *reinterpret_cast<const f32x4_t*>(partial + i);
+    for (int sp = 1; sp < splits; ++sp) s += *reinterpret_cast<const f32x4_t*>(partial + sp * MN + i);
+    store_out(Y, y_bf16, i, s);
 }
 
-// ---- launch plan ----------------------------------------------------------------
-struct SkinnyPlan {
-    int mt;          // 16-row blocks per wave tile (1, 2 or 4)
-    int64_t ntiles, mtiles;
+// ---- plans ---------------------------------------------------------------------
+// Per-M choices, measured on MI355X for K = 4096 and N = 14336 / 151936.
+using TileS = TileCfg<128, 128, 64, 32, 64>;   // 8 waves, M in (32, 256]
+using TileL = TileCfg<192, 256, 64, 96, 64>;   // 8 waves, M in (128, 192] with a wide N
+using TileB = TileCfg<256, 128, 64, 64, 64>;   // 8 waves, M > 256
+
+enum Kern { kStrip1, kStrip2, kTileS, kTileL, kTileB };
+
+struct Plan {
+    Kern kern;
+    int64_t mtiles, ntiles;
     int splits;
-    size_t partial_bytes, counter_bytes;
+    size_t ws_bytes;
 };
 
-SkinnyPlan plan_skinny(int64_t M, int64_t N, int64_t K) {
-    SkinnyPlan p;
-    p.mt = (M <= 16) ? 1 : (M <= 32) ? 2 : 4;
-    p.ntiles = (N + kNT - 1) / kNT;
-    p.mtiles = (M + 16 * p.mt - 1) / (16 * p.mt);
-    const int64_t nsteps = (K + kKS - 1) / kKS;
-    const int64_t tiles = p.ntiles * p.mtiles;
-    int64_t s = (1024 + tiles - 1) / tiles;                 // aim for >= 1024 workgroups
-    s = s < 1 ? 1 : s;
-    const int64_t smax = nsteps / (2 * kSkinnyWaves);       // >= 2 MFMA steps per wave
-    if (s > smax) s = smax < 1 ? 1 : smax;
-    if (s > 32) s = 32;
-    p.splits = (int)s;
-    const int64_t Mp = p.mtiles * 16 * p.mt;
-    p.partial_bytes = p.splits > 1 ? align_up((size_t)p.splits * Mp * N * sizeof(float), 256) : 0;
-    p.counter_bytes = p.splits > 1 ? align_up((size_t)tiles * sizeof(int32_t), 256) : 0;
+Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
+    Plan p{};
+    if (M <= 32) {
+        p.kern = M <= 16 ? kStrip1 : kStrip2;
+        const int mt = M <= 16 ? 1 : 2;
+        p.mtiles = (M + 16 * mt - 1) / (16 * mt);
+        p.ntiles = (N + kStripN - 1) / kStripN;
+        p.splits = 1;
+        p.ws_bytes = 0;
+        return p;
+    }
+    int BM, BN, BK;
+    if (M > 128 && M <= 192 && (N + TileL::BN - 1) / TileL::BN >= cus) {
+        p.kern = kTileL; BM = TileL::BM; BN = TileL::BN; BK = TileL::BK;
+    } else if (M <= 256) {
+        p.kern = kTileS; BM = TileS::BM; BN = TileS::BN; BK = TileS::BK;
+    } else {
+        p.kern = kTileB; BM = TileB::BM; BN = TileB::BN; BK = TileB::BK;
+    }
+    p.mtiles = (M + BM - 1) / BM;
+    p.ntiles = (N + BN - 1) / BN;
+    const int64_t tiles = p.mtiles * p.ntiles;
+    const int64_t nst = (K + BK - 1) / BK;
+    // split K in two when the tiles alone leave more than half the machine idle
+    p.splits = (2 * tiles <= cus && nst >= 8) ? 2 : 1;
+    p.ws_bytes = p.splits > 1 ? align_up((size_t)p.splits * M * N * sizeof(float), 256) : 0;
     return p;
+}
+
+int device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 256;
+    return cus > 0 ? cus : 256;
+}
+
+template <typename Cfg, int D>
+int launch_tile(const Plan& p, const uint16_t* x, const uint16_t* w, void* Y, int yb, int64_t M,
+                int64_t N, int64_t K, float* partial, hipStream_t s) {
+    constexpr size_t lds = 2 * Cfg::LDS;
+    if constexpr (lds > 65536) {
+        if (hipFuncSetAttribute((const void*)k_tile<Cfg, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds) != hipSuccess)
+            return SPEC_ERR_HIP;
+    }
+    hipLaunchKernelGGL((k_tile<Cfg, D>), dim3((unsigned)p.mtiles, (unsigned)p.ntiles, (unsigned)p.splits),
+                       dim3(Cfg::NT), lds, s, x, w, Y, yb, M, N, K, p.splits, partial);
+    if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+    if (p.splits > 1) {
+        const int64_t MN = M * N;
+        const int64_t nthr = MN / 4;
+        hipLaunchKernelGGL(k_reduce, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s, partial,
+                           Y, yb, MN, p.splits);
+        if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+    }
+    return SPEC_OK;
 }
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -292,8 +529,7 @@ using namespace specv;
 
 extern "C" size_t spec_verify_linear_workspace_bytes(int64_t M, int64_t N, int64_t Kd) {
     if (M <= 0 || N <= 0 || Kd <= 0) return 0;
-    const SkinnyPlan p = plan_skinny(M, N, Kd);
-    return p.partial_bytes + p.counter_bytes;
+    return make_plan(M, N, Kd, device_cus()).ws_bytes;
 }
 
 extern "C" int spec_verify_linear(const void* X, const void* W, void* Y, int y_dtype, int64_t M,
@@ -303,31 +539,23 @@ extern "C" int spec_verify_linear(const void* X, const void* W, void* Y, int y_d
     if (y_dtype != SPEC_F32 && y_dtype != SPEC_BF16) return SPEC_ERR_INVALID_ARG;
     if (M == 0) return SPEC_OK;
     if (!X || !W || !Y || !aligned16(X) || !aligned16(W) || !aligned16(Y)) return SPEC_ERR_INVALID_ARG;
-    const SkinnyPlan p = plan_skinny(M, N, Kd);
+    const Plan p = make_plan(M, N, Kd, device_cus());
     if (p.ntiles > 65535 || p.mtiles > 0x7FFFFFFF) return SPEC_ERR_INVALID_ARG;
-    const size_t need = p.partial_bytes + p.counter_bytes;
-    if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace)))
+    if (p.ws_bytes > 0 && (!workspace || workspace_bytes < p.ws_bytes || !aligned16(workspace)))
         return SPEC_ERR_WORKSPACE;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    float* partial = need ? static_cast<float*>(workspace) : nullptr;
-    int32_t* counters = need ? reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + p.partial_bytes) : nullptr;
-    if (counters) {
-        // tile counters start at zero (a fill kernel, not a memset node, so
-        // that the call can be captured in a HIP graph)
-        const int64_t n = p.ntiles * p.mtiles;
-        hipLaunchKernelGGL(k_zero_i32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, counters, n);
-        if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-    }
-    const dim3 grid((unsigned)p.mtiles, (unsigned)p.ntiles, (unsigned)p.splits);
-    const dim3 block(kSkinnyWaves * kWave);
-    const size_t lds = 0;
     const uint16_t* x = static_cast<const uint16_t*>(X);
     const uint16_t* w = static_cast<const uint16_t*>(W);
     const int yb = y_dtype == SPEC_BF16;
-    switch (p.mt) {
-        case 1: hipLaunchKernelGGL(k_skinny<1>, grid, block, lds, s, x, w, Y, yb, M, N, Kd, p.splits, partial, counters); break;
-        case 2: hipLaunchKernelGGL(k_skinny<2>, grid, block, lds, s, x, w, Y, yb, M, N, Kd, p.splits, partial, counters); break;
-        default: hipLaunchKernelGGL(k_skinny<4>, grid, block, lds, s, x, w, Y, yb, M, N, Kd, p.splits, partial, counters); break;
+    float* partial = static_cast<float*>(workspace);
+    const dim3 sgrid((unsigned)p.mtiles, (unsigned)p.ntiles);
+    const dim3 sblock(kStripWaves * kWave);
+    switch (p.kern) {
+        case kStrip1: hipLaunchKernelGGL(k_strip<1>, sgrid, sblock, 0, s, x, w, Y, yb, M, N, Kd); break;
+        case kStrip2: hipLaunchKernelGGL(k_strip<2>, sgrid, sblock, 0, s, x, w, Y, yb, M, N, Kd); break;
+        case kTileS: return launch_tile<TileS, 2>(p, x, w, Y, yb, M, N, Kd, partial, s);
+        case kTileL: return launch_tile<TileL, 2>(p, x, w, Y, yb, M, N, Kd, partial, s);
+        case kTileB: return launch_tile<TileB, 2>(p, x, w, Y, yb, M, N, Kd, partial, s);
     }
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
     return SPEC_OK;
