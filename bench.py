@@ -59,7 +59,7 @@ def bench_step(torch, sv, workloads, steps, warmup):
     g = torch.Generator(device=dev)
     g.manual_seed(2005)
     q, x, L = workloads.draft_side_device(z3, K, 1.0, 0.6, g)
-    ws_acc = torch.empty(sv.accept_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+    ws_acc = sv.accept_workspace(B, K, V, dev)
     out = sv.AcceptResult(torch.empty(B, K + 1, dtype=torch.int32, device=dev),
                           torch.empty(B, dtype=torch.int32, device=dev),
                           torch.empty(B, K, dtype=torch.float32, device=dev),
@@ -104,7 +104,7 @@ def bench_accept_large(torch, sv, workloads, reps=60, nsets=5):
     dev = torch.device("cuda:0")
     B, K, V = 64, 7, 128256
     sets = [workloads.large_accept_device(3000 + s, dev) for s in range(nsets)]
-    ws = torch.empty(sv.accept_workspace_bytes(B, K, V), dtype=torch.uint8, device=dev)
+    ws = sv.accept_workspace(B, K, V, dev)
     outs = [sv.AcceptResult(torch.empty(B, K + 1, dtype=torch.int32, device=dev),
                             torch.empty(B, dtype=torch.int32, device=dev),
                             torch.empty(B, K, dtype=torch.float32, device=dev),

@@ -52,6 +52,10 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 #define SPEC_ROW_ZERO_Q 8      /* q_i(x_i) not > 0 at a position < L_b (stochastic mode) */
 #define SPEC_ROW_RESID_ZERO 16 /* informational: the residual max(p - q, 0) summed to 0,
                                   the token was drawn from p instead */
+#define SPEC_ROW_STALLED 32    /* the row's workgroups did not all make progress within the
+                                  wait bound (about 0.1 s); out_accepted[b] = -1, the rest
+                                  of the row's outputs are unspecified, and the workspace
+                                  must be zero-filled again before its next use */
 
 /* Limits. */
 #define SPEC_MAX_DRAFT 255 /* K <= 255 */
@@ -90,7 +94,8 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
  *                  q_i(x_i) is validated; q rows must hold probabilities.
  *   draft_tokens   [B, K] int32 (may be NULL iff K == 0)
  *   draft_lens     [B] int32 L_b in [0, K], or NULL meaning every L_b = K
- *   B, K, V        rows (>= 0), max draft length (0..SPEC_MAX_DRAFT), vocab (>= 1)
+ *   B, K, V        rows (>= 0), max draft length (0..SPEC_MAX_DRAFT), vocab
+ *                  (1 .. 4194304 for fp32 logits, .. 8388608 for bf16)
  *   row_base       global index of row 0 (>= 0, row_base + B <= 2^32): the
  *                  Philox stream of row b is that of global row row_base + b,
  *                  so a batch split into row shards reproduces the unsplit call
@@ -103,8 +108,13 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
  *                  invalid rows
  *   out_status     [B] int32 or NULL: SPEC_ROW_* bits
  *   workspace      device scratch of at least spec_accept_workspace_bytes(B, K, V)
- *                  bytes (its contents need not be initialised; it is
- *                  clobbered)
+ *                  bytes, 16-byte aligned.  Its first 256 * B bytes hold
+ *                  per-row counters through which the workgroups of a row
+ *                  hand work to one another: they must be ZERO when the call
+ *                  starts, and every call leaves them zero again.  So a
+ *                  workspace zero-filled once serves every later call with
+ *                  the same or fewer rows (any K, V).  Calls that may run
+ *                  concurrently need separate workspaces.
  * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP.
  * B == 0 returns SPEC_OK without launching.
  * ---------------------------------------------------------------------- */

@@ -29,6 +29,7 @@ ROW_BAD_TOKEN = 2
 ROW_BAD_LEN = 4
 ROW_ZERO_Q = 8
 ROW_RESID_ZERO = 16
+ROW_STALLED = 32
 MAX_DRAFT = 255
 
 # (name, restype, argtypes) for every entry point declared in the header
@@ -109,6 +110,12 @@ def accept_workspace_bytes(B: int, K: int, V: int) -> int:
     return int(load_library().spec_accept_workspace_bytes(B, K, V))
 
 
+def accept_workspace(B: int, K: int, V: int, device) -> torch.Tensor:
+    """A zero-filled workspace for spec_accept (the library keeps it zeroed
+    from call to call; reuse it for calls of the same or smaller size)."""
+    return torch.zeros(max(accept_workspace_bytes(B, K, V), 1), dtype=torch.uint8, device=device)
+
+
 def linear_workspace_bytes(M: int, N: int, Kd: int) -> int:
     return int(load_library().spec_verify_linear_workspace_bytes(M, N, Kd))
 
@@ -157,9 +164,8 @@ def accept(target_logits, draft_probs, draft_tokens, draft_lens=None, *, tempera
                            torch.empty(B, dtype=torch.int32, device=dev),
                            torch.empty(B, K, dtype=torch.float32, device=dev),
                            torch.empty(B, dtype=torch.int32, device=dev))
-    need = lib.spec_accept_workspace_bytes(B, K, V)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        workspace = accept_workspace(B, K, V, dev)
     rc = lib.spec_accept(
         _ptr(target_logits), dt, _ptr(draft_probs), _ptr(draft_tokens), _ptr(draft_lens),
         B, K, V, row_base, float(temperature), seed & (2**64 - 1), offset & (2**64 - 1),

@@ -18,7 +18,9 @@ __device__ __forceinline__ PhiloxBlock philox4x32_10(uint32_t c0, uint32_t c1, u
                                                      uint32_t c3, uint32_t k0, uint32_t k1) {
     constexpr uint32_t kMulA = 0xD2511F53u, kMulB = 0xCD9E8D57u;
     constexpr uint32_t kWeylA = 0x9E3779B9u, kWeylB = 0xBB67AE85u;
-#pragma unroll
+    // rolled: the generator runs a few times per row, off the streaming path,
+    // where a small code footprint matters more than loop overhead
+#pragma unroll 1
     for (int r = 0; r < 10; ++r) {
         const uint32_t pa_hi = __umulhi(kMulA, c0), pa_lo = kMulA * c0;
         const uint32_t pb_hi = __umulhi(kMulB, c2), pb_lo = kMulB * c2;

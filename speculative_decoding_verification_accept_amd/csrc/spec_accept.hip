@@ -11,83 +11,140 @@
 // speculative decoding beats it" (trefon.com), section "Speculative
 // decoding" (acceptance rule, greedy longest-prefix rule).
 //
-// The vocabulary is cut into chunks of 4096 entries.  Three launches on the
-// caller's stream (two in greedy mode); kernel boundaries order the phases,
-// so no workgroup ever waits on, or fences for, another:
-//  1. k_stats: single-wave workgroups walk a compact list of (row, position
-//     <= L_b, chunk) items (the lengths are prefix-summed in registers), each
-//     streaming its 4096 logits from HBM with 16-byte coalesced loads while
-//     the next item's loads are already in flight.  Per chunk: max m, then
-//     sum_j 2^(fl(z_j c - fl(m c))) with c = log2(e)/T (one FMA and one
-//     v_exp_f32 per entry), wave64 butterflies, fp64 across lanes.  Greedy
-//     mode keeps (max, lowest index) instead.
-//  2. k_decide: one workgroup per (row, chunk).  Each merges the row's chunk
-//     partials (fixed order, fp64), runs the acceptance tests (p_i(x_i) in
-//     fp64) and finds the first rejection a_b; after a rejection it computes
-//     the residual mass sum max(p - q, 0) of its chunk.
-//  3. k_sample: one workgroup per row.  Two-level inverse CDF: chunk masses
-//     (residual, or p-frame masses from launch 1 for the bonus token) pick
-//     the chunk, then one LDS-staged fp64 scan of that chunk picks the token.
+// One launch.  The vocabulary is cut into chunks of 16 KB of logits (8192
+// bf16 or 4096 fp32 entries) and one 256-thread workgroup owns one (row b,
+// chunk) pair; the C workgroups of a row have consecutive indices.
+//  phase 1  the workgroup streams its chunk of the logits at every verified
+//           position i <= L_b (16-byte coalesced loads; the next position's
+//           loads are in flight while the current one is reduced) and
+//           publishes, per position, the chunk max m and
+//           sum_j 2^(fl(z_j c - fl(m c))) with c = fl(log2(e) / T): one FMA and
+//           one v_exp_f32 per entry, fp64 across lanes (greedy mode: the max
+//           and its lowest index).  The workgroup whose chunk holds draft
+//           token x_i also gathers z_i(x_i) and q_i(x_i).
+//  decide   the last of the row's workgroups to finish phase 1 merges the
+//           partials of each position in a fixed order (fp64), runs the
+//           acceptance tests, finds the first rejection a_b and publishes
+//           the decision.  Greedy mode writes the row's outputs here.
+//  phase 2  every workgroup of the row waits for the decision, then publishes
+//           its chunk's mass at position a_b: the residual sum of
+//           max(p - q, 0) after a rejection, the p-mass for the bonus token.
+//  sample   the last of the row's workgroups to publish its mass draws the
+//           token by inverse CDF: the chunk masses pick the chunk, then one
+//           LDS-staged fp64 scan of that chunk picks the token.
+// Rows do not wait for one another: a row with short drafts is in phase 2
+// while longer rows still stream phase 1.
+//
+// Exchange between workgroups of one launch.  Every word one workgroup
+// publishes for another is written and read with agent-scope atomic
+// accesses, which gfx950 issues with the SC1 bit: the store goes through to
+// the device's coherence point and the load is served from it, so the eight
+// per-XCD L2 caches never hand out a stale copy.  Before a workgroup counts
+// itself in on a row counter it waits for its own stores to complete
+// (s_waitcnt vmcnt(0)), so the workgroup that sees the final count also sees
+// every published word.  The decision, which waiting workgroups poll, is
+// two words with a tag bit each.  The per-row records (two counters and the
+// decision words, 256 bytes per row, at the start of the workspace) must be
+// zero when a call starts; the workgroup that consumes a record last resets
+// it, so a workspace zeroed once stays valid for every later call with the
+// same or fewer rows.  Each record has cache lines of its own: device-scope
+// atomics on one line serialise.
+//
+// Progress.  A workgroup waits only for the decision of its own row, which
+// needs only phase 1 of that row's workgroups, and phase 1 never waits.
+// Workgroups are dispatched in index order, so the lowest unfinished row
+// always has all of its workgroups resident.  Each wait is bounded anyway:
+// past the bound the workgroup marks its row SPEC_ROW_STALLED and exits.
+//
 // No floating-point atomics: every reduction runs in a fixed order, so the
-// output is a deterministic function of the inputs.
+// outputs are a deterministic function of the inputs.
 #include "spec_verify.h"
 #include "device_common.hpp"
 #include "philox.hpp"
 
 #include <math.h>
 
-#include <atomic>
-
 namespace specv {
-int64_t resident_waves(const void* kernel);
 namespace {
 
-constexpr int kChunk = 4096;                 // vocabulary entries per chunk
-constexpr int kWEPT = kChunk / kWave;        // entries per lane in k_stats (64)
-constexpr int kThreads = 256;                // k_decide / k_sample workgroups
-constexpr int kTEPT = kChunk / kThreads;     // entries per thread there (16)
+constexpr int kThreads = 256;                // one workgroup per (row, chunk)
+constexpr int kChunkBytes = 16384;           // logits bytes per chunk
 constexpr int kWaves = kThreads / kWave;
-constexpr int kRegLens = 4;                  // lengths held in registers by k_stats
-constexpr int kCompactMaxB = kWave * kRegLens;
-constexpr int kSampleRegs = 4;               // chunk weights held per thread by k_sample
+// Entries per chunk and per thread: 8192 bf16 or 4096 fp32 logits.
+template <typename T> constexpr int chunk_of() { return kChunkBytes / (int)sizeof(T); }
+template <typename T> constexpr int ept_of() { return chunk_of<T>() / kThreads; }
+constexpr int kMinChunk = kChunkBytes / 4;   // the smallest chunk (fp32), for sizing
+constexpr int kPos = SPEC_MAX_DRAFT + 1;     // positions per row at most
+constexpr int kMaxChunks = 1024;             // chunks per row at most (the sampler keeps their masses in LDS)
+constexpr int kMergeRegs = 2;                // chunk partials held per lane by the merge
+constexpr int kSpinLimit = 1 << 16;          // polls of one wait (~0.1 s) before giving up
+constexpr int kRowStride = 64;               // ints per row-counter record: 256 bytes
 constexpr int kInvalidMask = SPEC_ROW_NONFINITE | SPEC_ROW_BAD_TOKEN | SPEC_ROW_BAD_LEN | SPEC_ROW_ZERO_Q;
-
-struct StatPart {  // stochastic partial of one (row, position, chunk)
-    float m;       // chunk max
-    int flag;      // 1: NaN or +Inf in the chunk
-    double s;      // sum_j 2^(fl(z_j c - fl(m c)))
-};
-struct ArgPart {  // greedy partial
-    float v;
-    int flag;
-    int idx;
-    int pad;
-};
-struct RowInfo {  // k_decide -> k_sample
-    int a;        // first rejection (or L_b)
-    int status;   // SPEC_ROW_* bits
-    int reject;   // a < L_b
-    float M;      // max logit at position a
-    double S;     // p-frame normaliser at position a (frame fl(M c))
-    double pad;
-};
-static_assert(sizeof(StatPart) == 16 && sizeof(ArgPart) == 16 && sizeof(RowInfo) == 32, "layout");
 
 typedef uint16_t bf16_t;
 
-// ---- loaders -----------------------------------------------------------------
-// Vector width (entries per 16-byte load) of each logits layout.
+// Row-counter record (zero between calls): [0] phase-1 arrivals,
+// [16] phase-2 arrivals, [32..35] the two tagged decision words.
+constexpr int kCnt1 = 0, kCnt2 = 16, kDec = 32;
+
+// ---- exchange between workgroups -----------------------------------------------
+__device__ __forceinline__ void co_store(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t co_load(const uint64_t* p) {
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void co_store32(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int co_add(int* p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Wait until every memory operation this wave has issued has completed
+// (vmcnt = 0; expcnt and lgkmcnt left at their maxima).
+__device__ __forceinline__ void drain_vm() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+__device__ __forceinline__ uint64_t pack2(float lo, uint32_t hi) {
+    return (uint64_t)__float_as_uint(lo) | ((uint64_t)hi << 32);
+}
+__device__ __forceinline__ uint64_t dbits(double d) { return (uint64_t)__double_as_longlong(d); }
+__device__ __forceinline__ double bitsd(uint64_t u) { return __longlong_as_double((long long)u); }
+
+// ---- partials --------------------------------------------------------------------
+// Stochastic partial of one (row, position, chunk): word 0 = chunk max m
+// (low half) and a flag (high half: 1 = NaN or +Inf in the chunk); word 1 =
+// fp64 sum_j 2^(fl(z_j c - fl(m c))).  Greedy partial: word 0 = max value
+// and flag, word 1 = lowest index of the max.
+struct StatPart {
+    float m;
+    int flag;
+    double s;
+};
+__device__ __forceinline__ void publish_part(uint64_t* p, float m, int flag, uint64_t w1) {
+    co_store(p, pack2(m, (uint32_t)flag));
+    co_store(p + 1, w1);
+}
+__device__ __forceinline__ StatPart read_part(const uint64_t* p) {
+    const uint64_t w0 = co_load(p), w1 = co_load(p + 1);
+    return StatPart{__uint_as_float((uint32_t)w0), (int)(w0 >> 32), bitsd(w1)};
+}
+
+// ---- loaders ---------------------------------------------------------------------
 template <typename T, bool VEC> struct Lay { static constexpr int W = 1; };
 template <> struct Lay<bf16_t, true> { static constexpr int W = 8; };
 template <> struct Lay<float, true> { static constexpr int W = 4; };
 
-// "Strided" layout over NT threads: vector k of thread t is vector
-// (k * NT + t) of the chunk, so consecutive threads read consecutive 16-byte
-// vectors.  Register e of thread t holds entry
-//   chunk0 + ((e / W) * NT + t) * W + e % W.
-template <int W, int NT>
+// "Strided" layout over the workgroup: vector k of thread t is vector
+// (k * kThreads + t) of the chunk, so consecutive threads read consecutive
+// 16-byte vectors.  Register e of thread t holds entry
+//   chunk0 + ((e / W) * kThreads + t) * W + e % W.
+template <int W>
 __device__ __forceinline__ int64_t strided_index(int64_t chunk0, int t, int e) {
-    return chunk0 + ((int64_t)(e / W) * NT + t) * W + (e % W);
+    return chunk0 + ((int64_t)(e / W) * kThreads + t) * W + (e % W);
 }
 
 __device__ __forceinline__ void unpack8(const uint4 w, float* v) {
@@ -97,22 +154,23 @@ __device__ __forceinline__ void unpack8(const uint4 w, float* v) {
     v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
 }
 
-// One thread's share of a chunk in strided layout, kept as loaded (raw
-// 16-byte vectors) so that loads can stay in flight until the values are used.
-template <typename T, bool VEC, int NT, int EPT> struct Raw;
+// One thread's share of a chunk of logits in strided layout, kept as loaded
+// so that loads stay in flight until the values are used.  Entries past V
+// read as -inf.
+template <typename T, bool VEC, int EPT> struct Raw;
 
-template <int NT, int EPT> struct Raw<bf16_t, true, NT, EPT> {
+template <int EPT> struct Raw<bf16_t, true, EPT> {
     uint4 r[EPT / 8];
     __device__ __forceinline__ void load(const bf16_t* row, int64_t V, int64_t chunk0, int t) {
         const uint4* p = reinterpret_cast<const uint4*>(row + chunk0) + t;
-        if (chunk0 + (int64_t)NT * EPT <= V) {  // whole chunk in range (uniform)
+        if (chunk0 + EPT * kThreads <= V) {  // whole chunk in range (uniform)
 #pragma unroll
-            for (int k = 0; k < EPT / 8; ++k) r[k] = p[k * NT];
+            for (int k = 0; k < EPT / 8; ++k) r[k] = p[k * kThreads];
         } else {
 #pragma unroll
             for (int k = 0; k < EPT / 8; ++k)
-                r[k] = (chunk0 + ((int64_t)k * NT + t) * 8 < V)
-                           ? p[k * NT]
+                r[k] = (chunk0 + ((int64_t)k * kThreads + t) * 8 < V)
+                           ? p[k * kThreads]
                            : make_uint4(0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u, 0xFF80FF80u);
         }
     }
@@ -122,18 +180,18 @@ template <int NT, int EPT> struct Raw<bf16_t, true, NT, EPT> {
     }
 };
 
-template <int NT, int EPT> struct Raw<float, true, NT, EPT> {
+template <int EPT> struct Raw<float, true, EPT> {
     float4 r[EPT / 4];
     __device__ __forceinline__ void load(const float* row, int64_t V, int64_t chunk0, int t) {
         const float4* p = reinterpret_cast<const float4*>(row + chunk0) + t;
-        if (chunk0 + (int64_t)NT * EPT <= V) {  // whole chunk in range (uniform)
+        if (chunk0 + EPT * kThreads <= V) {
 #pragma unroll
-            for (int k = 0; k < EPT / 4; ++k) r[k] = p[k * NT];
+            for (int k = 0; k < EPT / 4; ++k) r[k] = p[k * kThreads];
         } else {
 #pragma unroll
             for (int k = 0; k < EPT / 4; ++k)
-                r[k] = (chunk0 + ((int64_t)k * NT + t) * 4 < V)
-                           ? p[k * NT]
+                r[k] = (chunk0 + ((int64_t)k * kThreads + t) * 4 < V)
+                           ? p[k * kThreads]
                            : make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
         }
     }
@@ -145,12 +203,12 @@ template <int NT, int EPT> struct Raw<float, true, NT, EPT> {
     }
 };
 
-template <typename T, int NT, int EPT> struct Raw<T, false, NT, EPT> {
+template <typename T, int EPT> struct Raw<T, false, EPT> {
     float r[EPT];
     __device__ __forceinline__ void load(const T* row, int64_t V, int64_t chunk0, int t) {
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            const int64_t j = chunk0 + (int64_t)e * NT + t;
+            const int64_t j = chunk0 + (int64_t)e * kThreads + t;
             float x = -INFINITY;
             if (j < V) {
                 if constexpr (sizeof(T) == 2) x = bf16_to_f32(row[j]);
@@ -165,20 +223,20 @@ template <typename T, int NT, int EPT> struct Raw<T, false, NT, EPT> {
     }
 };
 
-// q entries in the same order as Raw<T, VEC, NT, EPT>; 0 past V.
-template <typename T, bool VEC, int NT, int EPT>
+// q entries in the same order as Raw<T, VEC, EPT>; 0 past V.
+template <typename T, bool VEC, int EPT>
 __device__ __forceinline__ void load_q_strided(const float* row, int64_t V, int64_t chunk0, int t,
                                                float (&v)[EPT]) {
     constexpr int W = Lay<T, VEC>::W;
     if constexpr (W > 1) {
         const float4* p = reinterpret_cast<const float4*>(row + chunk0) + (int64_t)t * (W / 4);
-        const bool full = chunk0 + (int64_t)NT * EPT <= V;  // uniform
+        const bool full = chunk0 + EPT * kThreads <= V;  // uniform
 #pragma unroll
         for (int k = 0; k < EPT / W; ++k) {
-            const bool ok = full || chunk0 + ((int64_t)k * NT + t) * W < V;
+            const bool ok = full || chunk0 + ((int64_t)k * kThreads + t) * W < V;
 #pragma unroll
             for (int h = 0; h < W / 4; ++h) {
-                const float4 f = ok ? p[(int64_t)k * NT * (W / 4) + h] : make_float4(0.f, 0.f, 0.f, 0.f);
+                const float4 f = ok ? p[(int64_t)k * kThreads * (W / 4) + h] : make_float4(0.f, 0.f, 0.f, 0.f);
                 v[k * W + 4 * h] = f.x; v[k * W + 4 * h + 1] = f.y;
                 v[k * W + 4 * h + 2] = f.z; v[k * W + 4 * h + 3] = f.w;
             }
@@ -186,7 +244,7 @@ __device__ __forceinline__ void load_q_strided(const float* row, int64_t V, int6
     } else {
 #pragma unroll
         for (int e = 0; e < EPT; ++e) {
-            const int64_t j = chunk0 + (int64_t)e * NT + t;
+            const int64_t j = chunk0 + (int64_t)e * kThreads + t;
             v[e] = (j < V) ? row[j] : 0.f;
         }
     }
@@ -255,7 +313,6 @@ __device__ __forceinline__ float r_weight(float z, float q, float c, float mc, f
     const float p = p_weight(z, c, mc) * invS;
     return fmaxf(p - q, 0.f);
 }
-
 // p-frame mass of one chunk partial relative to the position's fl(M c).
 __device__ __forceinline__ double chunk_p_mass(const StatPart& e, float c, float mcM) {
     if (e.m == -INFINITY) return 0.0;
@@ -264,15 +321,33 @@ __device__ __forceinline__ double chunk_p_mass(const StatPart& e, float c, float
 }
 
 // ---- workgroup reductions -------------------------------------------------------
+__device__ __forceinline__ float block_max(float v, float* sh) {
+    v = wave_max(v);
+    if ((threadIdx.x & (kWave - 1)) == 0) sh[threadIdx.x / kWave] = v;
+    __syncthreads();
+    float r = sh[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) r = fmaxf(r, sh[k]);
+    return r;
+}
+// Fixed-order workgroup sum; the total is valid in every thread.  The caller
+// separates consecutive uses of one `sh` with a barrier.
 __device__ __forceinline__ double block_sum(double v, double* sh) {
     v = wave_sum(v);
-    const int w = threadIdx.x / kWave;
-    if ((threadIdx.x & (kWave - 1)) == 0) sh[w] = v;
+    if ((threadIdx.x & (kWave - 1)) == 0) sh[threadIdx.x / kWave] = v;
     __syncthreads();
     double r = sh[0];
 #pragma unroll
     for (int k = 1; k < kWaves; ++k) r += sh[k];
+    return r;
+}
+__device__ __forceinline__ int block_or(int v, int* sh) {
+    v = wave_or(v);
+    if ((threadIdx.x & (kWave - 1)) == 0) sh[threadIdx.x / kWave] = v;
     __syncthreads();
+    int r = sh[0];
+#pragma unroll
+    for (int k = 1; k < kWaves; ++k) r |= sh[k];
     return r;
 }
 
@@ -299,141 +374,233 @@ __device__ __forceinline__ double block_incl_scan(double v, double* sh, double* 
     return base + v;
 }
 
-__device__ __forceinline__ int wave_incl_scan_int(int v) {
-    const int lane = threadIdx.x & (kWave - 1);
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int n = __shfl_up(v, o, kWave);
-        if (lane >= o) v += n;
-    }
-    return v;
-}
-
 // Merge of the C chunk partials of one position by one wave (lanes over
-// chunks, butterfly reductions: a fixed order).  Every kernel that needs a
-// position's (M, S) calls this, so they all see the same bits.
+// chunks, butterfly reductions: a fixed order).
 struct PosStats {
     float M;
     double S;
     int flag;
 };
-__device__ __forceinline__ PosStats merge_position(const StatPart* pp, int C, float c) {
+__device__ __forceinline__ PosStats merge_position(const uint64_t* pp, int C, float c) {
     const int lane = threadIdx.x & (kWave - 1);
+    StatPart e[kMergeRegs];
     float M = -INFINITY;
     int flag = 0;
-    for (int k = lane; k < C; k += kWave) {
-        M = fmaxf(M, pp[k].m);
-        flag |= pp[k].flag;
+#pragma unroll
+    for (int r = 0; r < kMergeRegs; ++r) {
+        const int k = lane + r * kWave;
+        e[r] = (k < C) ? read_part(pp + 2 * k) : StatPart{-INFINITY, 0, 0.0};
+        M = fmaxf(M, e[r].m);
+        flag |= e[r].flag;
+    }
+    for (int k = lane + kMergeRegs * kWave; k < C; k += kWave) {
+        const StatPart x = read_part(pp + 2 * k);
+        M = fmaxf(M, x.m);
+        flag |= x.flag;
     }
     M = wave_max(M);
     flag = wave_or(flag);
     if (M == -INFINITY || M == INFINITY) flag = 1;
     const float mcM = M * c;
     double S = 0.0;
-    if (!flag)
-        for (int k = lane; k < C; k += kWave) S += chunk_p_mass(pp[k], c, mcM);
+    if (!flag) {
+#pragma unroll
+        for (int r = 0; r < kMergeRegs; ++r) S += chunk_p_mass(e[r], c, mcM);
+        for (int k = lane + kMergeRegs * kWave; k < C; k += kWave) S += chunk_p_mass(read_part(pp + 2 * k), c, mcM);
+    }
     S = wave_sum(S);
     return PosStats{M, S, flag};
 }
 
-// ---- launch 1: chunk statistics ----------------------------------------------------
-// Work list of (row-position rp = b (K+1) + i, chunk).  For B <= 256 the
-// list is compact: lane l holds n_b = L_b + 1 (0 for a bad length) for
-// b = l + 64 j, prefix-summed across the wave, and item w maps to
-// position pos = w / C of the concatenated valid positions.  Larger batches
-// walk all B (K+1) positions and skip those past L_b.
-struct WorkList {
-    int pst[kRegLens];  // exclusive prefix of n_b, b = lane + 64 j
-    int64_t B;
-    int K, C;
-    bool compact;
-    const int32_t* lens;
-    int64_t nitems;
+// Greedy merge: (max value, lowest index) over the chunk partials.
+__device__ __forceinline__ void merge_argmax(const uint64_t* pp, int C, float& bv, int& bi, int& flag) {
+    const int lane = threadIdx.x & (kWave - 1);
+    bv = -INFINITY;
+    bi = 0x7FFFFFFF;
+    flag = 0;
+    for (int k = lane; k < C; k += kWave) {
+        const uint64_t w0 = co_load(pp + 2 * k), w1 = co_load(pp + 2 * k + 1);
+        const float v = __uint_as_float((uint32_t)w0);
+        const int idx = (int)w1;
+        flag |= (int)(w0 >> 32);
+        if (v > bv || (v == bv && idx < bi)) { bv = v; bi = idx; }
+    }
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, kWave);
+        const int oi = __shfl_xor(bi, o, kWave);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+    }
+    flag = wave_or(flag);
+    if (bv == -INFINITY || bv == INFINITY) flag = 1;
+}
 
-    __device__ __forceinline__ void init(const int32_t* lens_, int64_t B_, int K_, int C_) {
-        lens = lens_;
-        B = B_;
-        K = K_;
-        C = C_;
-        compact = B <= kCompactMaxB;
-        if (compact) {
-            const int lane = threadIdx.x & (kWave - 1);
-            int carry = 0;
+// ---- decision words ------------------------------------------------------------------
+// word 0: bit 0 tag, bit 1 reject, bits 2..9 status, bits 10..17 a_b,
+//         bits 32..63 M (max logit at a_b);  word 1: bit 0 tag, bits 32..63 fl(1/S)
+struct Decision {
+    int a, status, reject;
+    float M, invS;
+};
+__device__ __forceinline__ uint64_t dec_word0(const Decision& d) {
+    return 1ull | ((uint64_t)(d.reject & 1) << 1) | ((uint64_t)(d.status & 0xFF) << 2) |
+           ((uint64_t)(d.a & 0xFF) << 10) | ((uint64_t)__float_as_uint(d.M) << 32);
+}
+__device__ __forceinline__ uint64_t dec_word1(const Decision& d) {
+    return 1ull | ((uint64_t)__float_as_uint(d.invS) << 32);
+}
+__device__ __forceinline__ Decision dec_read(uint64_t w0, uint64_t w1) {
+    return Decision{(int)((w0 >> 10) & 0xFF), (int)((w0 >> 2) & 0xFF), (int)((w0 >> 1) & 1),
+                    __uint_as_float((uint32_t)(w0 >> 32)), __uint_as_float((uint32_t)(w1 >> 32))};
+}
+
+// ---- draw weights at the chosen position ---------------------------------------------
+// Weight of entry j: the residual max(p - q, 0) after a rejection (qrow set),
+// the p-frame weight otherwise; 0 past V.
+template <typename T>
+__device__ __forceinline__ float entry_weight(const T* zrow, const float* qrow, int64_t V, int64_t j,
+                                              float c, float mcM, float invS) {
+    if (j >= V) return 0.f;
+    const float z = load_one(zrow, j);
+    return qrow ? r_weight(z, qrow[j], c, mcM, invS) : p_weight(z, c, mcM);
+}
+// Sum, in index order and fp64, of the weights of entries [start, start + EPT):
+// the same per-entry expressions as entry_weight.
+template <typename T, bool VEC, int EPT>
+__device__ __forceinline__ double thread_weight_sum(const T* zrow, const float* qrow, int64_t V,
+                                                    int64_t start, float c, float mcM, float invS) {
+    float z[EPT];
+    load_contig<T, VEC, EPT>(zrow, V, start, z);
+    double own = 0.0;
+    if (qrow) {
+        float qq[EPT];
+        load_q_contig<VEC, EPT>(qrow, V, start, qq);
 #pragma unroll
-            for (int j = 0; j < kRegLens; ++j) {
-                const int64_t b = lane + kWave * j;
-                int n = 0;
-                if (b < B) {
-                    const int L = lens ? lens[b] : K;
-                    n = (L >= 0 && L <= K) ? L + 1 : 0;
-                }
-                const int incl = wave_incl_scan_int(n);
-                pst[j] = carry + incl - n;
-                carry += __shfl(incl, kWave - 1, kWave);
-            }
-            nitems = (int64_t)carry * C;
-        } else {
-            nitems = B * (K + 1) * C;
-        }
-    }
-    // item w -> (rp, chunk); false if the item is past L_b (non-compact only)
-    __device__ __forceinline__ bool locate(int64_t w, int64_t& rp, int& ci) const {
-        const int64_t pos = w / C;
-        ci = (int)(w % C);
-        if (compact) {
-            const int lane = threadIdx.x & (kWave - 1);
-            int cnt = 0;
+        for (int e = 0; e < EPT; ++e) own += (double)r_weight(z[e], qq[e], c, mcM, invS);
+    } else {
 #pragma unroll
-            for (int j = 0; j < kRegLens; ++j)
-                cnt += __popcll(__ballot((lane + kWave * j < B) && (int64_t)pst[j] <= pos));
-            const int b = cnt - 1;
-            const int j = b / kWave;
-            static_assert(kRegLens == 4, "select chain below");
-            const int sel = (j == 0) ? pst[0] : (j == 1) ? pst[1] : (j == 2) ? pst[2] : pst[3];
-            const int base = __shfl(sel, b % kWave, kWave);
-            rp = (int64_t)b * (K + 1) + (pos - base);
-            return true;
-        }
-        rp = pos;
-        const int64_t b = rp / (K + 1);
-        const int i = (int)(rp % (K + 1));
-        const int L = lens ? lens[b] : K;
-        return L >= 0 && L <= K && i <= L;
+        for (int e = 0; e < EPT; ++e) own += (double)p_weight(z[e], c, mcM);
     }
-    // first valid item at or after w in steps of `stride`
-    __device__ __forceinline__ bool next(int64_t& w, int64_t stride, int64_t& rp, int& ci) const {
-        while (w < nitems) {
-            if (locate(w, rp, ci)) return true;
-            w += stride;
-        }
-        return false;
+    return own;
+}
+
+// Inclusive scan of one double per lane across a wave.
+__device__ __forceinline__ double wave_incl_scan(double v) {
+    const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double n = __shfl_up(v, o, kWave);
+        if (lane >= o) v += n;
     }
+    return v;
+}
+
+// ---- the kernel -----------------------------------------------------------------------------
+struct Args {
+    const void* logits;
+    const float* q;
+    const int32_t* tokens;
+    const int32_t* lens;
+    int64_t B, V, row_base;
+    int K, C;
+    float c;  // log2(e) / T (stochastic)
+    uint64_t seed, offset;
+    int32_t* out_tokens;
+    int32_t* out_accepted;
+    float* out_p_draft;
+    int32_t* out_status;
+    int* rows;       // row-counter records, kRowStride ints per row
+    uint64_t* part;  // [B][K+1][C] two words each
+    uint64_t* gath;  // [B][K] z_i(x_i) | q_i(x_i) << 32
+    uint64_t* mass;  // [B][C] fp64 chunk masses at a_b
+    uint64_t* tsum;  // [B][C][kThreads] fp64 per-thread weight sums at a_b
 };
 
+struct Shared {
+    float red_f[kWaves];
+    double red_d[kWaves];
+    int red_i[kWaves];
+    float red_v[kWaves];
+    int red_x[kWaves];
+    StatPart own[kPos];  // this workgroup's partial at each position
+    union {
+        struct {  // decide
+            float M[kPos];
+            double S[kPos];
+            int flag[kPos];
+            float px[kPos];
+            int gi[kPos];
+        } d;
+        struct {  // sample
+            double w[kMaxChunks];  // chunk masses
+            double scan[kThreads + 1];
+        } s;
+    } u;
+    double tp;
+    int status, a, last, cstar, lastpos;
+    uint64_t w0, w1;
+};
+
+template <typename T, bool VEC>
+__device__ void write_invalid_row(const Args& g, int64_t b, int status, int t) {
+    for (int i = t; i <= g.K; i += kThreads) g.out_tokens[b * (g.K + 1) + i] = -1;
+    if (g.out_p_draft)
+        for (int i = t; i < g.K; i += kThreads) g.out_p_draft[b * g.K + i] = -1.f;
+    if (t == 0) {
+        g.out_accepted[b] = -1;
+        if (g.out_status) g.out_status[b] = status;
+    }
+}
+
 template <typename T, bool VEC, bool GREEDY>
-__global__ __launch_bounds__(kWave) void k_stats(const T* __restrict__ logits,
-                                                 const int32_t* __restrict__ lens, int64_t B, int K,
-                                                 int64_t V, int C, float c, void* __restrict__ part_out) {
+__global__ __launch_bounds__(kThreads) void k_accept(Args g) {
     constexpr int W = Lay<T, VEC>::W;
-    const int lane = threadIdx.x;
-    WorkList wl;
-    wl.init(lens, B, K, C);
-    const int64_t stride = gridDim.x;
-    auto process = [&](const Raw<T, VEC, kWave, kWEPT>& raw, int64_t rp, int ci) {
-        float v[kWEPT];
+    constexpr int EPT = ept_of<T>(), CH = chunk_of<T>();
+    __shared__ Shared sh;
+    const T* logits = static_cast<const T*>(g.logits);
+    const int64_t b = blockIdx.x / g.C;
+    const int ci = (int)(blockIdx.x % g.C);
+    const int t = threadIdx.x;
+    const int lane = t & (kWave - 1);
+    const int wv = t / kWave;
+    const int K = g.K, C = g.C;
+    const int64_t V = g.V;
+    const float c = g.c;
+    int* rowc = g.rows + b * kRowStride;
+
+    const int L = g.lens ? g.lens[b] : K;
+    if (L < 0 || L > K) {  // no counter of this row is touched
+        if (ci == 0) write_invalid_row<T, VEC>(g, b, SPEC_ROW_BAD_LEN, t);
+        return;
+    }
+    const int64_t chunk0 = (int64_t)ci * CH;
+    const T* zrow0 = logits + b * (K + 1) * V;
+
+    // draft token of position t (t < L); the owner of its chunk gathers
+    // z_t(x_t) and q_t(x_t) for the acceptance test
+    const int x = (t < L) ? g.tokens[b * K + t] : -1;
+    if (!GREEDY && t < L && x >= 0 && (int64_t)x < V && x / CH == ci) {
+        const float zx = load_one(zrow0 + (int64_t)t * V, x);
+        const float qx = g.q[(b * K + t) * V + x];
+        co_store(g.gath + b * K + t, pack2(zx, __float_as_uint(qx)));
+    }
+
+    // ---- phase 1: chunk statistics at every position i <= L ----
+    uint64_t* prow = g.part + (b * (K + 1)) * C * 2;
+    auto reduce = [&](const Raw<T, VEC, EPT>& raw, int i) {
+        float v[EPT];
         raw.unpack(v);
-        const int64_t pidx = rp * C + ci;
+        uint64_t* pp = prow + ((int64_t)i * C + ci) * 2;
         if constexpr (GREEDY) {
-            const int64_t chunk0 = (int64_t)ci * kChunk;
             float best = -INFINITY;
             int bidx = 0x7FFFFFFF, nan = 0;
 #pragma unroll
-            for (int e = 0; e < kWEPT; ++e) {
-                const int64_t j = strided_index<W, kWave>(chunk0, lane, e);
-                const float x = v[e];
+            for (int e = 0; e < EPT; ++e) {
+                const int64_t j = strided_index<W>(chunk0, t, e);
+                const float xv = v[e];
                 if (j < V) {
-                    nan |= (x != x);
-                    if (x > best || (x == best && (int)j < bidx)) { best = x; bidx = (int)j; }
+                    nan |= (xv != xv);
+                    if (xv > best || (xv == best && (int)j < bidx)) { best = xv; bidx = (int)j; }
                 }
             }
 #pragma unroll
@@ -443,16 +610,31 @@ __global__ __launch_bounds__(kWave) void k_stats(const T* __restrict__ logits,
                 if (ov > best || (ov == best && oi < bidx)) { best = ov; bidx = oi; }
             }
             nan = wave_or(nan);
-            if (lane == 0)
-                static_cast<ArgPart*>(part_out)[pidx] = ArgPart{best, (nan || best == INFINITY) ? 1 : 0, bidx, 0};
+            if (lane == 0) {
+                sh.red_v[wv] = best;
+                sh.red_x[wv] = bidx;
+                sh.red_i[wv] = nan;
+            }
+            __syncthreads();
+            if (t == 0) {
+                float bv = sh.red_v[0];
+                int bi = sh.red_x[0], fl = sh.red_i[0];
+#pragma unroll
+                for (int k = 1; k < kWaves; ++k) {
+                    fl |= sh.red_i[k];
+                    if (sh.red_v[k] > bv || (sh.red_v[k] == bv && sh.red_x[k] < bi)) { bv = sh.red_v[k]; bi = sh.red_x[k]; }
+                }
+                publish_part(pp, bv, (fl || bv == INFINITY) ? 1 : 0, (uint64_t)(uint32_t)bi);
+            }
+            __syncthreads();
         } else {
             float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < kWEPT; e += 2) {
+            for (int e = 0; e < EPT; e += 2) {
                 m0 = fmaxf(m0, v[e]);
                 m1 = fmaxf(m1, v[e + 1]);
             }
-            const float m = wave_max(fmaxf(m0, m1));
+            const float m = block_max(fmaxf(m0, m1), sh.red_f);
             int flag = 0;
             double s = 0.0;
             if (m == INFINITY) {
@@ -460,471 +642,333 @@ __global__ __launch_bounds__(kWave) void k_stats(const T* __restrict__ logits,
             } else if (m == -INFINITY) {
                 int nan = 0;
 #pragma unroll
-                for (int e = 0; e < kWEPT; ++e) nan |= (v[e] != v[e]);
-                flag = wave_or(nan);
+                for (int e = 0; e < EPT; ++e) nan |= (v[e] != v[e]);
+                flag = block_or(nan, sh.red_i);
             } else {
                 const float mc = m * c;
                 float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
 #pragma unroll
-                for (int e = 0; e < kWEPT; e += 4) {
+                for (int e = 0; e < EPT; e += 4) {
                     a0 += p_weight(v[e], c, mc);
                     a1 += p_weight(v[e + 1], c, mc);
                     a2 += p_weight(v[e + 2], c, mc);
                     a3 += p_weight(v[e + 3], c, mc);
                 }
-                s = wave_sum((double)((a0 + a1) + (a2 + a3)));
+                s = block_sum((double)((a0 + a1) + (a2 + a3)), sh.red_d);
                 flag = (s != s) ? 1 : 0;
             }
-            if (lane == 0) static_cast<StatPart*>(part_out)[pidx] = StatPart{m, flag, s};
+            if (t == 0) {
+                publish_part(pp, m, flag, dbits(s));
+                sh.own[i] = StatPart{m, flag, s};
+            }
+            __syncthreads();  // separates this position's reductions from the next
         }
     };
-    // two register buffers in ping-pong: the next item's loads are issued
-    // before the current item is reduced
-    Raw<T, VEC, kWave, kWEPT> bufA, bufB;
-    int64_t w = blockIdx.x, rpA = 0, rpB = 0;
-    int ciA = 0, ciB = 0;
-    bool haveA = wl.next(w, stride, rpA, ciA);
-    if (haveA) bufA.load(logits + rpA * V, V, (int64_t)ciA * kChunk, lane);
-    while (haveA) {
-        int64_t w2 = w + stride;
-        const bool haveB = wl.next(w2, stride, rpB, ciB);
-        if (haveB) bufB.load(logits + rpB * V, V, (int64_t)ciB * kChunk, lane);
-        process(bufA, rpA, ciA);
-        if (!haveB) break;
-        w = w2 + stride;
-        haveA = wl.next(w, stride, rpA, ciA);
-        if (haveA) bufA.load(logits + rpA * V, V, (int64_t)ciA * kChunk, lane);
-        process(bufB, rpB, ciB);
+    {
+        Raw<T, VEC, EPT> buf0, buf1;
+        buf0.load(zrow0, V, chunk0, t);
+        if (L >= 1) buf1.load(zrow0 + V, V, chunk0, t);
+        for (int i = 0; i <= L; i += 2) {
+            reduce(buf0, i);
+            if (i + 2 <= L) buf0.load(zrow0 + (int64_t)(i + 2) * V, V, chunk0, t);
+            if (i + 1 > L) break;
+            reduce(buf1, i + 1);
+            if (i + 3 <= L) buf1.load(zrow0 + (int64_t)(i + 3) * V, V, chunk0, t);
+        }
     }
-}
 
-// ---- launch 2: decisions and residual chunk masses ----------------------------------
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_decide(
-    const T* __restrict__ logits, const float* __restrict__ q, const int32_t* __restrict__ tokens,
-    const int32_t* __restrict__ lens, int K, int64_t V, int C, float c, int64_t row_base,
-    uint64_t seed, uint64_t offset, const StatPart* __restrict__ part, double* __restrict__ resid,
-    RowInfo* __restrict__ info, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ out_accepted, float* __restrict__ out_p_draft,
-    int32_t* __restrict__ out_status) {
-    constexpr int kPos = SPEC_MAX_DRAFT + 1;
-    __shared__ float s_M[kPos];
-    __shared__ double s_S[kPos];
-    __shared__ int s_flag[kPos];
-    __shared__ float s_zx[kPos];
-    __shared__ float s_qx[kPos];
-    __shared__ float s_px[kPos];
-    __shared__ double sh_d[kWaves];
-    __shared__ int s_status, s_a;
-
-    const int64_t b = blockIdx.x / C;
-    const int ci = (int)(blockIdx.x % C);
-    const int t = threadIdx.x;
-    const int lane = t & (kWave - 1);
-    const int wv = t / kWave;
-    const int x = (t < K) ? tokens[b * K + t] : 0;  // issued with the length load
-    const int L = lens ? lens[b] : K;
-    const bool len_ok = (L >= 0 && L <= K);
-    if (t == 0) {
-        s_status = len_ok ? 0 : SPEC_ROW_BAD_LEN;
-        s_a = len_ok ? L : 0;
-    }
+    // count in on the row; the last workgroup decides
+    drain_vm();
+    __syncthreads();
+    if (t == 0) sh.last = (co_add(rowc + kCnt1, 1) == C - 1);
     __syncthreads();
 
-    // gather z_i(x_i) and q_i(x_i) of every drafted position (one thread each)
-    if (len_ok && t < L) {
-        int st = 0;
-        float zx = 0.f, qx = 1.f;
-        if (x < 0 || (int64_t)x >= V) {
-            st = SPEC_ROW_BAD_TOKEN;
-        } else {
-            zx = load_one(logits + (b * (K + 1) + t) * V, x);
-            qx = q[(b * K + t) * V + x];
-            if (!(qx > 0.f)) st = SPEC_ROW_ZERO_Q;
+    if (sh.last) {
+        // ---- decide ----
+        if (t == 0) {
+            co_store32(rowc + kCnt1, 0);
+            sh.status = 0;
+            sh.a = L;
         }
-        s_zx[t] = zx;
-        s_qx[t] = qx;
-        if (st) atomicOr(&s_status, st);
-    }
-    // merge the chunk partials of each position <= L_b, one wave per position
-    if (len_ok) {
-        for (int i = wv; i <= L; i += kWaves) {
-            const PosStats ps = merge_position(part + (b * (K + 1) + i) * C, C, c);
-            if (lane == 0) {
-                s_M[i] = ps.M;
-                s_S[i] = ps.S;
-                s_flag[i] = ps.flag;
-                if (ps.flag) atomicOr(&s_status, SPEC_ROW_NONFINITE);
+        __syncthreads();
+        if constexpr (GREEDY) {
+            for (int i = wv; i <= L; i += kWaves) {
+                float bv;
+                int bi, fl;
+                merge_argmax(prow + (int64_t)i * C * 2, C, bv, bi, fl);
+                if (lane == 0) {
+                    sh.u.d.gi[i] = bi;
+                    if (fl) atomicOr(&sh.status, SPEC_ROW_NONFINITE);
+                }
             }
-        }
-    }
-    __syncthreads();
-    // acceptance tests, then the first rejection
-    if (len_ok && t < L) {
-        float px = -1.f;
-        int rej = 0;
-        const float qx = s_qx[t];
-        if (!s_flag[t] && qx > 0.f) {
-            const float mcM = s_M[t] * c;
-            const double p = exp2((double)s_zx[t] * (double)c - (double)mcM) / s_S[t];
-            px = (float)p;
-            const double a = fmin(1.0, p / (double)qx);
-            const RowPosUniforms u = row_pos_uniforms(seed, offset, (uint32_t)(row_base + b), (uint32_t)t);
-            rej = ((double)u.acc < a) ? 0 : 1;
-        }
-        s_px[t] = px;
-        if (rej) atomicMin(&s_a, t);
-    }
-    __syncthreads();
-    const int status = s_status;
-    const int a = s_a;
-    const bool invalid = (status & kInvalidMask) != 0;
-    const bool reject = !invalid && a < L;
-    if (ci == 0) {
-        if (out_p_draft)
-            for (int i = t; i < K; i += kThreads)
-                out_p_draft[b * K + i] = (!invalid && i < L) ? s_px[i] : -1.f;
-        if (invalid) {
-            for (int i = t; i <= K; i += kThreads) out_tokens[b * (K + 1) + i] = -1;
+            if (t < L && (x < 0 || (int64_t)x >= V)) atomicOr(&sh.status, SPEC_ROW_BAD_TOKEN);
+            __syncthreads();
+            if (t < L && x != sh.u.d.gi[t]) atomicMin(&sh.a, t);
+            __syncthreads();
+            const int status = sh.status, a = sh.a;
+            const bool invalid = (status & kInvalidMask) != 0;
+            if (g.out_p_draft)
+                for (int i = t; i < K; i += kThreads)
+                    g.out_p_draft[b * K + i] = (!invalid && i < L) ? (g.tokens[b * K + i] == sh.u.d.gi[i] ? 1.f : 0.f) : -1.f;
+            for (int i = t; i <= K; i += kThreads) {
+                int v = -1;
+                if (!invalid) {
+                    if (i < a) v = g.tokens[b * K + i];
+                    else if (i == a) v = sh.u.d.gi[a];
+                }
+                g.out_tokens[b * (K + 1) + i] = v;
+            }
             if (t == 0) {
-                out_accepted[b] = -1;
-                if (out_status) out_status[b] = status;
+                g.out_accepted[b] = invalid ? -1 : a;
+                if (g.out_status) g.out_status[b] = status;
+            }
+            return;
+        } else {
+            // gathers and token checks (one thread per drafted position)
+            float zx = 0.f, qx = 1.f;
+            if (t < L) {
+                int st = 0;
+                if (x < 0 || (int64_t)x >= V) {
+                    st = SPEC_ROW_BAD_TOKEN;
+                } else {
+                    const uint64_t gw = co_load(g.gath + b * K + t);
+                    zx = __uint_as_float((uint32_t)gw);
+                    qx = __uint_as_float((uint32_t)(gw >> 32));
+                    if (!(qx > 0.f)) st = SPEC_ROW_ZERO_Q;
+                }
+                if (st) atomicOr(&sh.status, st);
+            }
+            for (int i = wv; i <= L; i += kWaves) {
+                const PosStats ps = merge_position(prow + (int64_t)i * C * 2, C, c);
+                if (lane == 0) {
+                    sh.u.d.M[i] = ps.M;
+                    sh.u.d.S[i] = ps.S;
+                    sh.u.d.flag[i] = ps.flag;
+                    if (ps.flag) atomicOr(&sh.status, SPEC_ROW_NONFINITE);
+                }
+            }
+            __syncthreads();
+            if (t < L) {
+                float px = -1.f;
+                int rej = 0;
+                if (!sh.u.d.flag[t] && qx > 0.f) {
+                    const float mcM = sh.u.d.M[t] * c;
+                    const double p = exp2((double)zx * (double)c - (double)mcM) / sh.u.d.S[t];
+                    px = (float)p;
+                    const double acc = fmin(1.0, p / (double)qx);
+                    const RowPosUniforms u = row_pos_uniforms(g.seed, g.offset, (uint32_t)(g.row_base + b), (uint32_t)t);
+                    rej = ((double)u.acc < acc) ? 0 : 1;
+                }
+                sh.u.d.px[t] = px;
+                if (rej) atomicMin(&sh.a, t);
+            }
+            __syncthreads();
+            const int status = sh.status, a = sh.a;
+            const bool invalid = (status & kInvalidMask) != 0;
+            if (g.out_p_draft)
+                for (int i = t; i < K; i += kThreads)
+                    g.out_p_draft[b * K + i] = (!invalid && i < L) ? sh.u.d.px[i] : -1.f;
+            if (invalid) write_invalid_row<T, VEC>(g, b, status, t);
+            if (t == 0) {
+                Decision d{invalid ? 0 : a, status, (!invalid && a < L) ? 1 : 0,
+                           invalid ? 0.f : sh.u.d.M[a], invalid ? 0.f : (float)(1.0 / sh.u.d.S[a])};
+                const uint64_t w0 = dec_word0(d), w1 = dec_word1(d);
+                co_store(reinterpret_cast<uint64_t*>(rowc + kDec), w0);
+                co_store(reinterpret_cast<uint64_t*>(rowc + kDec) + 1, w1);
+                sh.w0 = w0;
+                sh.w1 = w1;
             }
         }
-        if (t == 0) info[b] = RowInfo{a, status, reject ? 1 : 0, invalid ? 0.f : s_M[a], invalid ? 0.0 : s_S[a], 0.0};
+    } else {
+        if constexpr (GREEDY) return;
+        // ---- wait for the row's decision ----
+        if (t == 0) {
+            const uint64_t* dw = reinterpret_cast<const uint64_t*>(rowc + kDec);
+            uint64_t w0 = 0, w1 = 0;
+            int n = 0;
+            for (;;) {
+                w0 = co_load(dw);
+                w1 = co_load(dw + 1);
+                if (w0 & w1 & 1) break;
+                if (++n >= kSpinLimit) break;
+                __builtin_amdgcn_s_sleep(8);
+            }
+            sh.w0 = w0;
+            sh.w1 = w1;
+        }
     }
-    if (invalid) return;
-    const float mcM = s_M[a] * c;
-    if (!reject) {
-        // the bonus draw uses the p-frame mass of each chunk at position a
-        if (t == 0) resid[b * C + ci] = chunk_p_mass(part[(b * (K + 1) + a) * C + ci], c, mcM);
+    __syncthreads();
+    if (!(sh.w0 & sh.w1 & 1)) {  // the bound ran out: give up on the row
+        if (t == 0) {
+            g.out_accepted[b] = -1;
+            if (g.out_status) g.out_status[b] = SPEC_ROW_STALLED;
+        }
         return;
     }
+    const Decision d = dec_read(sh.w0, sh.w1);
+    const bool invalid = (d.status & kInvalidMask) != 0;
+    const int a = d.a;
+    const float mcM = d.M * c;
 
-    // residual mass of this chunk at the rejected position
-    const float invS = (float)(1.0 / s_S[a]);
-    const T* zrow = logits + (b * (K + 1) + a) * V;
-    const float* qrow = q + (b * K + a) * V;
-    const int64_t chunk0 = (int64_t)ci * kChunk;
-    Raw<T, VEC, kThreads, kTEPT> raw;
-    raw.load(zrow, V, chunk0, t);
-    float qq[kTEPT], z[kTEPT];
-    load_q_strided<T, VEC, kThreads, kTEPT>(qrow, V, chunk0, t, qq);
-    raw.unpack(z);
-    float r0 = 0.f, r1 = 0.f, r2 = 0.f, r3 = 0.f;
-#pragma unroll
-    for (int e = 0; e < kTEPT; e += 4) {
-        r0 += r_weight(z[e], qq[e], c, mcM, invS);
-        r1 += r_weight(z[e + 1], qq[e + 1], c, mcM, invS);
-        r2 += r_weight(z[e + 2], qq[e + 2], c, mcM, invS);
-        r3 += r_weight(z[e + 3], qq[e + 3], c, mcM, invS);
+    // ---- phase 2: this chunk's draw weights at position a ----
+    // Thread t sums the weights of entries [chunk0 + t EPT, + EPT) and
+    // publishes that sum (the sampler's second level) and the chunk's total
+    // (its first level).
+    const T* zrow = zrow0 + (int64_t)a * V;
+    const float* qrow = d.reject ? g.q + (b * K + a) * V : nullptr;
+    uint64_t* tsrow = g.tsum + b * C * kThreads;  // [C][kThreads]
+    double mass = 0.0;
+    if (!invalid) {
+        const double own = thread_weight_sum<T, VEC, EPT>(zrow, qrow, V, chunk0 + (int64_t)t * EPT, c, mcM, d.invS);
+        co_store(tsrow + (int64_t)ci * kThreads + t, dbits(own));
+        mass = block_sum(own, sh.red_d);
     }
-    const double R = block_sum((double)((r0 + r1) + (r2 + r3)), sh_d);
-    if (t == 0) resid[b * C + ci] = R;
-}
+    if (t == 0) co_store(g.mass + b * C + ci, dbits(mass));
+    drain_vm();
+    __syncthreads();
+    if (t == 0) sh.last = (co_add(rowc + kCnt2, 1) == C - 1);
+    __syncthreads();
+    if (!sh.last) return;
 
-// ---- launch 3: the categorical draw ------------------------------------------------------
-template <typename T, bool VEC>
-__global__ __launch_bounds__(kThreads) void k_sample(
-    const T* __restrict__ logits, const float* __restrict__ q, const int32_t* __restrict__ tokens,
-    int K, int64_t V, int C, float c, int64_t row_base, uint64_t seed, uint64_t offset,
-    const StatPart* __restrict__ part, const double* __restrict__ resid,
-    const RowInfo* __restrict__ info, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ out_accepted, int32_t* __restrict__ out_status) {
-    __shared__ double sh_d[kWaves];
-    __shared__ double s_scan[kThreads + 1];
-    __shared__ double s_tp;
-    __shared__ int s_cstar, s_tok, s_lastpos;
-
-    const int64_t b = blockIdx.x;
-    const int t = threadIdx.x;
-    // the row's chunk weights and its decision record load together
-    double wreg[kSampleRegs];
-#pragma unroll
-    for (int j = 0; j < kSampleRegs; ++j) {
-        const int k = j * kThreads + t;
-        wreg[j] = (k < C) ? resid[b * C + k] : 0.0;
-    }
-    const RowInfo ri = info[b];
-    if (ri.status & kInvalidMask) return;  // k_decide wrote this row
-    const int a = ri.a;
-    int status = ri.status;
-    const StatPart* pp = part + (b * (K + 1) + a) * C;
+    // ---- sample (the row's last workgroup) ----
+    // Every workgroup of the row has counted in, so none reads the row's
+    // record again: reset it for the next call.
     if (t == 0) {
-        s_cstar = 0x7FFFFFFF;
-        s_tok = 0x7FFFFFFF;
-        s_lastpos = -1;
+        co_store32(rowc + kCnt2, 0);
+        co_store(reinterpret_cast<uint64_t*>(rowc + kDec), 0);
+        co_store(reinterpret_cast<uint64_t*>(rowc + kDec) + 1, 0);
     }
-    const float mcM = ri.M * c;
-    const float invS = (float)(1.0 / ri.S);
-    const T* zrow = logits + (b * (K + 1) + a) * V;
-    const float* qrow = ri.reject ? q + (b * K + a) * V : nullptr;
+    if (invalid) return;  // the decider wrote the row
+    int status = d.status;
+    int pmode = d.reject ? 0 : 1;  // 0: residual, 1: bonus from p, 2: empty residual, from p
+    const uint64_t* pa = prow + (int64_t)a * C * 2;
 
-    // first level: pick the chunk from the chunk masses (residual masses
-    // after a rejection, p-frame masses for the bonus token)
-    int pmode = ri.reject ? 0 : 1;
-    auto chunk_w = [&](int k) -> double {
-        if (k >= C) return 0.0;
-        const int j = k / kThreads;
-        if (pmode == 2 || j >= kSampleRegs) return (pmode == 2) ? chunk_p_mass(pp[k], c, mcM) : resid[b * C + k];
-        double r = wreg[0];
-#pragma unroll
-        for (int jj = 1; jj < kSampleRegs; ++jj) r = (j == jj) ? wreg[jj] : r;
-        return r;
-    };
-    double tot = 0.0;
-    for (int k0 = 0; k0 < C; k0 += kThreads) tot += block_sum(chunk_w(k0 + t), sh_d);
-    if (!pmode && !(tot > 0.0)) {  // residual is empty: draw from p
+    // level 1: the chunk.  Chunk masses go to LDS (C <= kMaxChunks); an empty
+    // residual is replaced by the p-frame masses of the position's partials.
+    for (int k = t; k < C; k += kThreads) sh.u.s.w[k] = bitsd(co_load(g.mass + b * C + k));
+    __syncthreads();
+    double tot;
+    for (;;) {
+        double part = 0.0;
+        for (int k = t; k < C; k += kThreads) part += sh.u.s.w[k];
+        tot = block_sum(part, sh.red_d);
+        __syncthreads();
+        if (pmode != 0 || tot > 0.0) break;
         pmode = 2;
         status |= SPEC_ROW_RESID_ZERO;
-        tot = 0.0;
-        for (int k0 = 0; k0 < C; k0 += kThreads) tot += block_sum(chunk_w(k0 + t), sh_d);
+        for (int k = t; k < C; k += kThreads) sh.u.s.w[k] = chunk_p_mass(read_part(pa + 2 * k), c, mcM);
+        __syncthreads();
     }
-    const RowPosUniforms u = row_pos_uniforms(seed, offset, (uint32_t)(row_base + b), (uint32_t)a);
-    const double tt = (double)u.smp * tot;
+    const RowPosUniforms u = row_pos_uniforms(g.seed, g.offset, (uint32_t)(g.row_base + b), (uint32_t)a);
+    double tp = (double)u.smp * tot;
+    if (t == 0) {
+        sh.cstar = -1;
+        sh.lastpos = -1;
+    }
     double carry = 0.0;
     for (int k0 = 0; k0 < C; k0 += kThreads) {
         const int k = k0 + t;
-        const double wk = chunk_w(k);
+        const double wk = (k < C) ? sh.u.s.w[k] : 0.0;
         double btot;
-        const double incl = carry + block_incl_scan(wk, sh_d, &btot);
-        s_scan[t + 1] = incl;
-        if (t == 0) s_scan[0] = carry;
+        const double incl = carry + block_incl_scan(wk, sh.red_d, &btot);
+        sh.u.s.scan[t + 1] = incl;
+        if (t == 0) sh.u.s.scan[0] = carry;
         __syncthreads();
-        if (k < C && wk > 0.0) {
-            atomicMax(&s_lastpos, k);
-            if (incl > tt && s_scan[t] <= tt) {
-                s_cstar = k;  // unique: the scan is non-decreasing
-                s_tp = tt - s_scan[t];
+        if (wk > 0.0) {
+            atomicMax(&sh.lastpos, k);
+            if (incl > tp && sh.u.s.scan[t] <= tp) {  // unique: the scan is non-decreasing
+                sh.cstar = k;
+                sh.tp = tp - sh.u.s.scan[t];
             }
         }
         __syncthreads();
-        if (s_cstar != 0x7FFFFFFF) break;
+        if (sh.cstar >= 0) break;
         carry += btot;
     }
-    int cstar = s_cstar;
-    double tp = s_tp;
-    if (cstar == 0x7FFFFFFF) {  // rounding left t at or past the total: last positive entry
-        cstar = s_lastpos;
+    int cstar = sh.cstar;
+    tp = sh.tp;
+    if (cstar < 0) {  // rounding left t at or past the total: the last positive chunk
+        cstar = max(sh.lastpos, 0);
         tp = INFINITY;
     }
     __syncthreads();
-    if (t == 0) s_lastpos = -1;
 
-    // second level: scan the chosen chunk in index order
-    const int64_t start = (int64_t)cstar * kChunk + (int64_t)t * kTEPT;
-    float w[kTEPT];
-    {
-        float z[kTEPT];
-        load_contig<T, VEC, kTEPT>(zrow, V, start, z);
-        if (pmode) {
-#pragma unroll
-            for (int e = 0; e < kTEPT; ++e) w[e] = p_weight(z[e], c, mcM);
-        } else {
-            float qq[kTEPT];
-            load_q_contig<VEC, kTEPT>(qrow, V, start, qq);
-#pragma unroll
-            for (int e = 0; e < kTEPT; ++e) w[e] = r_weight(z[e], qq[e], c, mcM, invS);
-        }
-    }
-    double own = 0.0;
-    int lastpos = -1;
-#pragma unroll
-    for (int e = 0; e < kTEPT; ++e) {
-        own += (double)w[e];
-        if (w[e] > 0.f) lastpos = e;
-    }
-    double ctot;
-    const double incl = block_incl_scan(own, sh_d, &ctot);
-    s_scan[t + 1] = incl;
-    if (t == 0) s_scan[0] = 0.0;
-    __syncthreads();
-    const double lo = s_scan[t], hi = s_scan[t + 1];
-    if (lo <= tp && tp < hi) {
-        double cum = lo;
-        int found = -1;
-#pragma unroll
-        for (int e = 0; e < kTEPT; ++e) {
-            cum += (double)w[e];
-            if (found < 0 && w[e] > 0.f && cum > tp) found = e;
-        }
-        if (found < 0) found = lastpos;
-        if (found >= 0) atomicMin(&s_tok, (int)(start + found));
-    }
-    if (lastpos >= 0) atomicMax(&s_lastpos, (int)(start + lastpos));
-    __syncthreads();
+    // level 2: the thread of chunk c* whose entries hold the draw
+    const int64_t cbase = (int64_t)cstar * CH;
+    const float* qdraw = pmode == 0 ? qrow : nullptr;
+    const double ts = (pmode == 2)
+                          ? thread_weight_sum<T, VEC, EPT>(zrow, nullptr, V, cbase + (int64_t)t * EPT, c, mcM, d.invS)
+                          : bitsd(co_load(tsrow + (int64_t)cstar * kThreads + t));
     if (t == 0) {
-        int tok = s_tok;
-        if (tok == 0x7FFFFFFF) tok = s_lastpos;  // t' at or past the chunk total
-        out_tokens[b * (K + 1) + a] = tok;
-        out_accepted[b] = a;
-        if (out_status) out_status[b] = status;
+        sh.cstar = -1;
+        sh.lastpos = -1;
+    }
+    double ttot;
+    const double incl2 = block_incl_scan(ts, sh.red_d, &ttot);
+    sh.u.s.scan[t + 1] = incl2;
+    if (t == 0) sh.u.s.scan[0] = 0.0;
+    __syncthreads();
+    if (ts > 0.0) {
+        atomicMax(&sh.lastpos, t);
+        if (incl2 > tp && sh.u.s.scan[t] <= tp) {
+            sh.cstar = t;
+            sh.tp = tp - sh.u.s.scan[t];
+        }
+    }
+    __syncthreads();
+    int tstar = sh.cstar;
+    tp = sh.tp;
+    if (tstar < 0) {
+        tstar = max(sh.lastpos, 0);
+        tp = INFINITY;
+    }
+
+    // level 3: that thread's EPT entries, one per lane of wave 0, in index order
+    if (wv == 0) {
+        const int64_t j0 = cbase + (int64_t)tstar * EPT;
+        const float wl = (lane < EPT) ? entry_weight(zrow, qdraw, V, j0 + lane, c, mcM, d.invS) : 0.f;
+        const double incl3 = wave_incl_scan((double)wl);
+        const uint64_t hit = __ballot(wl > 0.f && incl3 > tp);
+        const uint64_t pos = __ballot(wl > 0.f);
+        const int sel = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+        if (lane == 0) {
+            g.out_tokens[b * (K + 1) + a] = (int32_t)(j0 + sel);
+            g.out_accepted[b] = a;
+            if (g.out_status) g.out_status[b] = status;
+        }
     }
     for (int i = t; i <= K; i += kThreads)
-        if (i != a) out_tokens[b * (K + 1) + i] = (i < a) ? tokens[b * K + i] : -1;
-}
-
-// ---- greedy finish: one wave per row ---------------------------------------------------
-__global__ __launch_bounds__(kWave) void k_greedy_finish(
-    const int32_t* __restrict__ tokens, const int32_t* __restrict__ lens, int K, int64_t V, int C,
-    const ArgPart* __restrict__ part, int32_t* __restrict__ out_tokens,
-    int32_t* __restrict__ out_accepted, float* __restrict__ out_p_draft,
-    int32_t* __restrict__ out_status) {
-    __shared__ int s_g[SPEC_MAX_DRAFT + 1];
-    __shared__ int s_status, s_a;
-    const int64_t b = blockIdx.x;
-    const int t = threadIdx.x;
-    const int L = lens ? lens[b] : K;
-    const bool len_ok = (L >= 0 && L <= K);
-    if (t == 0) {
-        s_status = len_ok ? 0 : SPEC_ROW_BAD_LEN;
-        s_a = len_ok ? L : 0;
-    }
-    __syncthreads();
-    if (len_ok) {
-        // per position: lanes over chunks, butterfly (max value, lowest index)
-        for (int i = 0; i <= L; ++i) {
-            const ArgPart* pp = part + ((b * (K + 1) + i) * C);
-            float bv = -INFINITY;
-            int bi = 0x7FFFFFFF, flag = 0;
-            for (int k = t; k < C; k += kWave) {
-                const ArgPart e = pp[k];
-                flag |= e.flag;
-                if (e.v > bv || (e.v == bv && e.idx < bi)) { bv = e.v; bi = e.idx; }
-            }
-#pragma unroll
-            for (int o = kWave / 2; o > 0; o >>= 1) {
-                const float ov = __shfl_xor(bv, o, kWave);
-                const int oi = __shfl_xor(bi, o, kWave);
-                if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-            }
-            flag = wave_or(flag);
-            if (t == 0) {
-                s_g[i] = bi;
-                if (flag || bv == -INFINITY || bv == INFINITY) s_status |= SPEC_ROW_NONFINITE;
-            }
-        }
-        for (int i = t; i < L; i += kWave) {
-            const int x = tokens[b * K + i];
-            if (x < 0 || (int64_t)x >= V) atomicOr(&s_status, SPEC_ROW_BAD_TOKEN);
-        }
-    }
-    __syncthreads();
-    if (len_ok)
-        for (int i = t; i < L; i += kWave)
-            if (tokens[b * K + i] != s_g[i]) atomicMin(&s_a, i);
-    __syncthreads();
-    const int status = s_status;
-    const bool invalid = (status & kInvalidMask) != 0;
-    const int a = s_a;
-    if (out_p_draft)
-        for (int i = t; i < K; i += kWave)
-            out_p_draft[b * K + i] = (!invalid && i < L) ? (tokens[b * K + i] == s_g[i] ? 1.f : 0.f) : -1.f;
-    for (int i = t; i <= K; i += kWave) {
-        int v = -1;
-        if (!invalid) {
-            if (i < a) v = tokens[b * K + i];
-            else if (i == a) v = s_g[a];
-        }
-        out_tokens[b * (K + 1) + i] = v;
-    }
-    if (t == 0) {
-        out_accepted[b] = invalid ? -1 : a;
-        if (out_status) out_status[b] = status;
-    }
+        if (i != a) g.out_tokens[b * (K + 1) + i] = (i < a) ? g.tokens[b * K + i] : -1;
 }
 
 // ---- host side ------------------------------------------------------------------------------
 struct AcceptWs {
-    size_t part_off, resid_off, info_off, total;
+    size_t rows_off, part_off, gath_off, mass_off, tsum_off, total;
 };
 
 AcceptWs accept_ws_layout(int64_t B, int K, int64_t V) {
-    const int64_t C = (V + kChunk - 1) / kChunk;
+    const int64_t C = (V + kMinChunk - 1) / kMinChunk;  // the most chunks of either dtype
     AcceptWs w;
-    w.part_off = 0;
-    w.resid_off = align_up((size_t)B * (K + 1) * C * sizeof(StatPart), 256);
-    w.info_off = w.resid_off + align_up((size_t)B * C * sizeof(double), 256);
-    w.total = w.info_off + align_up((size_t)B * sizeof(RowInfo), 256);
+    w.rows_off = 0;
+    w.part_off = align_up((size_t)B * kRowStride * sizeof(int), 256);
+    w.gath_off = w.part_off + align_up((size_t)B * (K + 1) * C * 16, 256);
+    w.mass_off = w.gath_off + align_up((size_t)B * K * 8, 256);
+    w.tsum_off = w.mass_off + align_up((size_t)B * C * 8, 256);
+    w.total = w.tsum_off + align_up((size_t)B * C * kThreads * 8, 256);
     return w;
 }
 
 template <typename T, bool VEC>
-int launch_accept(const T* logits, const float* q, const int32_t* tokens, const int32_t* lens,
-                  int64_t B, int K, int64_t V, int64_t row_base, float temperature, uint64_t seed,
-                  uint64_t offset, int32_t* out_tokens, int32_t* out_accepted, float* out_p_draft,
-                  int32_t* out_status, char* ws, const AcceptWs& lay, hipStream_t stream) {
-    const int C = (int)((V + kChunk - 1) / kChunk);
-    const int64_t items = B * (K + 1) * C;
-    // k_stats is persistent: one generation of single-wave workgroups that
-    // fills the device, each walking several items
-    const int64_t cap = temperature == 0.f ? resident_waves((const void*)k_stats<T, VEC, true>)
-                                           : resident_waves((const void*)k_stats<T, VEC, false>);
-    if (cap <= 0) return SPEC_ERR_HIP;
-    const unsigned g1 = (unsigned)(items < cap ? items : cap);
-    void* part = ws + lay.part_off;
-    if (temperature == 0.f) {
-        hipLaunchKernelGGL((k_stats<T, VEC, true>), dim3(g1), dim3(kWave), 0, stream, logits, lens,
-                           B, K, V, C, 0.f, part);
-        if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-        hipLaunchKernelGGL(k_greedy_finish, dim3((unsigned)B), dim3(kWave), 0, stream, tokens, lens,
-                           K, V, C, static_cast<const ArgPart*>(part), out_tokens, out_accepted,
-                           out_p_draft, out_status);
-        if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-        return SPEC_OK;
-    }
-    // c = log2(e) / T, rounded once to fp32
-    const float c = (float)(1.4426950408889634074 / (double)temperature);
-    const StatPart* sp = static_cast<const StatPart*>(part);
-    double* resid = reinterpret_cast<double*>(ws + lay.resid_off);
-    RowInfo* info = reinterpret_cast<RowInfo*>(ws + lay.info_off);
-    hipLaunchKernelGGL((k_stats<T, VEC, false>), dim3(g1), dim3(kWave), 0, stream, logits, lens,
-                       B, K, V, C, c, part);
-    if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-    hipLaunchKernelGGL((k_decide<T, VEC>), dim3((unsigned)(B * C)), dim3(kThreads), 0, stream,
-                       logits, q, tokens, lens, K, V, C, c, row_base, seed, offset, sp, resid, info,
-                       out_tokens, out_accepted, out_p_draft, out_status);
-    if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-    hipLaunchKernelGGL((k_sample<T, VEC>), dim3((unsigned)B), dim3(kThreads), 0, stream, logits, q,
-                       tokens, K, V, C, c, row_base, seed, offset, sp, resid, info, out_tokens,
-                       out_accepted, out_status);
-    if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-    return SPEC_OK;
+int launch_accept(const Args& a, hipStream_t stream, bool greedy) {
+    const dim3 grid((unsigned)(a.B * a.C));
+    if (greedy) hipLaunchKernelGGL((k_accept<T, VEC, true>), grid, dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL((k_accept<T, VEC, false>), grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 }  // namespace
-
-// Number of single-wave workgroups of `kernel` the current device holds at
-// once (compute units x resident workgroups per unit); a read-only property
-// of the device and the code object, cached per (kernel, device).
-int64_t resident_waves(const void* kernel) {
-    constexpr int kMaxDev = 64, kMaxKernels = 16;
-    static std::atomic<int64_t> cache[kMaxKernels][kMaxDev];
-    static std::atomic<const void*> keys[kMaxKernels];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return -1;
-    int slot = -1;
-    for (int i = 0; i < kMaxKernels; ++i) {
-        const void* k = keys[i].load();
-        if (k == kernel) { slot = i; break; }
-        if (k == nullptr) {
-            const void* expect = nullptr;
-            if (keys[i].compare_exchange_strong(expect, kernel) || expect == kernel) { slot = i; break; }
-        }
-    }
-    if (slot >= 0 && dev < kMaxDev) {
-        const int64_t v = cache[slot][dev].load();
-        if (v > 0) return v;
-    }
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kWave, 0) != hipSuccess) return -1;
-    const int64_t v = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
-    if (slot >= 0 && dev < kMaxDev) cache[slot][dev].store(v);
-    return v;
-}
 }  // namespace specv
 
 using namespace specv;
@@ -949,32 +993,42 @@ extern "C" int spec_accept(const void* target_logits, int logits_dtype, const fl
     if (!target_logits || !out_tokens || !out_accepted) return SPEC_ERR_INVALID_ARG;
     if (K > 0 && !draft_tokens) return SPEC_ERR_INVALID_ARG;
     if (temperature > 0.f && K > 0 && !draft_probs) return SPEC_ERR_INVALID_ARG;
-    const int64_t C = (V + kChunk - 1) / kChunk;
-    // grid limit: k_decide has B*C workgroups
-    if (B * C > ((int64_t)1 << 24) || B * (K + 1) * C > ((int64_t)1 << 40)) return SPEC_ERR_INVALID_ARG;
+    const int64_t C = logits_dtype == SPEC_BF16 ? (V + chunk_of<bf16_t>() - 1) / chunk_of<bf16_t>()
+                                                : (V + chunk_of<float>() - 1) / chunk_of<float>();
+    // one workgroup per (row, chunk); the sampler holds a row's chunk masses in LDS
+    if (B * C > ((int64_t)1 << 24) || C > kMaxChunks) return SPEC_ERR_INVALID_ARG;
     const AcceptWs lay = accept_ws_layout(B, K, V);
     if (!workspace || workspace_bytes < lay.total || !aligned16(workspace)) return SPEC_ERR_WORKSPACE;
-    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     char* ws = static_cast<char*>(workspace);
-    const float* q = (temperature > 0.f) ? draft_probs : nullptr;
+    const bool greedy = temperature == 0.f;
+    Args a{};
+    a.logits = target_logits;
+    a.q = greedy ? nullptr : draft_probs;
+    a.tokens = draft_tokens;
+    a.lens = draft_lens;
+    a.B = B;
+    a.V = V;
+    a.row_base = row_base;
+    a.K = K;
+    a.C = (int)C;
+    // c = log2(e) / T, rounded once to fp32
+    a.c = greedy ? 0.f : (float)(1.4426950408889634074 / (double)temperature);
+    a.seed = philox_seed;
+    a.offset = philox_offset;
+    a.out_tokens = out_tokens;
+    a.out_accepted = out_accepted;
+    a.out_p_draft = out_p_draft;
+    a.out_status = out_status;
+    a.rows = reinterpret_cast<int*>(ws + lay.rows_off);
+    a.part = reinterpret_cast<uint64_t*>(ws + lay.part_off);
+    a.gath = reinterpret_cast<uint64_t*>(ws + lay.gath_off);
+    a.mass = reinterpret_cast<uint64_t*>(ws + lay.mass_off);
+    a.tsum = reinterpret_cast<uint64_t*>(ws + lay.tsum_off);
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     if (logits_dtype == SPEC_BF16) {
-        const bf16_t* z = static_cast<const bf16_t*>(target_logits);
-        const bool vec = (V % 8 == 0) && aligned16(z) && (!q || aligned16(q));
-        if (vec)
-            return launch_accept<bf16_t, true>(z, q, draft_tokens, draft_lens, B, K, V, row_base,
-                                               temperature, philox_seed, philox_offset, out_tokens,
-                                               out_accepted, out_p_draft, out_status, ws, lay, s);
-        return launch_accept<bf16_t, false>(z, q, draft_tokens, draft_lens, B, K, V, row_base,
-                                            temperature, philox_seed, philox_offset, out_tokens,
-                                            out_accepted, out_p_draft, out_status, ws, lay, s);
+        const bool vec = (V % 8 == 0) && aligned16(target_logits) && (!a.q || aligned16(a.q));
+        return vec ? launch_accept<bf16_t, true>(a, s, greedy) : launch_accept<bf16_t, false>(a, s, greedy);
     }
-    const float* z = static_cast<const float*>(target_logits);
-    const bool vec = (V % 4 == 0) && aligned16(z) && (!q || aligned16(q));
-    if (vec)
-        return launch_accept<float, true>(z, q, draft_tokens, draft_lens, B, K, V, row_base,
-                                          temperature, philox_seed, philox_offset, out_tokens,
-                                          out_accepted, out_p_draft, out_status, ws, lay, s);
-    return launch_accept<float, false>(z, q, draft_tokens, draft_lens, B, K, V, row_base,
-                                       temperature, philox_seed, philox_offset, out_tokens,
-                                       out_accepted, out_p_draft, out_status, ws, lay, s);
+    const bool vec = (V % 4 == 0) && aligned16(target_logits) && (!a.q || aligned16(a.q));
+    return vec ? launch_accept<float, true>(a, s, greedy) : launch_accept<float, false>(a, s, greedy);
 }
