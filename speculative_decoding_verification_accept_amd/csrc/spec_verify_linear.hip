@@ -1,5 +1,5 @@
 // spec_verify_linear.hip -- verify linear layer Y[M, N] = X[M, K] W[K, N] on
-// gfx950 bf16 MFMA (v_mfma_f32_16x16x32_bf16) with fp32 accumulation.
+// gfx950 bf16 MFMA with fp32 accumulation.
 //
 // Method: page "New technical post reveals how speculative decoding
 // accelerates LLM inference without hurting accuracy" (agentnet.co.il),
@@ -11,26 +11,28 @@
 // compute-bound.
 //
 // W is stored input-major ([K, N], N contiguous) while an MFMA operand wants
-// 8 consecutive k per lane.  Both kernels load W with row-contiguous 16- or
-// 8-byte loads and transpose small blocks in registers with v_perm_b32; X
-// (K contiguous) is used as stored.  The MFMA computes D = A B with A an X
-// fragment (16 rows m x 32 k) and B a W fragment (32 k x 16 columns n).
+// 8 consecutive k per lane; X (K contiguous) is used as stored.  The MFMA
+// computes D = A B with A an X fragment and B a W fragment.
 //
 //  k_strip (M <= 32, memory-bound): one 512-thread workgroup per 64-column
 //    strip of W, all M rows, the full K.  Each of its 8 waves takes a slice
 //    of K, keeps 4 k-steps of W loads in flight, transposes each lane's 8x4
-//    block straight into MFMA operands (no LDS for W), and the waves' partial
-//    tiles are summed through LDS in a fixed order.  W streams from HBM
-//    exactly once.
-//  k_tile (M > 32, v_mfma_f32_32x32x16_bf16): a workgroup computes a BM x BN
-//    tile.  Each K-stage of W
-//    is transposed in registers on its way into LDS ([n][k], k contiguous),
-//    X is staged as stored, and every wave reads its fragments from LDS, so
-//    one HBM read of W serves all BM rows; the next stage's global loads are
-//    in flight while the MFMAs of the current one run.  Split-K writes fp32
-//    partials that k_reduce sums in a fixed order (no atomics).
+//    block of W in registers (v_perm_b32) straight into
+//    v_mfma_f32_16x16x32_bf16 operands, and the waves' partial tiles are
+//    summed through LDS in a fixed order.  W streams from HBM exactly once.
+//  k_dma (M > 32, K a multiple of 32 or 64; v_mfma_f32_32x32x16_bf16): a
+//    workgroup computes a BM x BN tile.  Tiles of X and W go from HBM
+//    straight into an LDS ring of 4-5 stages by loads that write LDS, so the
+//    prefetch distance costs no registers; W stays [k][n] in LDS and the
+//    transposing LDS read ds_read_b64_tr_b16 builds its MFMA operands.
+//  k_tile (other K): the earlier design, W staged through registers and
+//    transposed with v_perm_b32 on its way into LDS.
+// Split-K (when the tiles alone fill less than half the machine) writes fp32
+// partials that k_reduce sums in a fixed order (no atomics).
 #include "spec_verify.h"
 #include "device_common.hpp"
+
+#include <utility>
 
 namespace specv {
 namespace {
@@ -437,6 +439,258 @@ __global__ __launch_bounds__(Cfg::NT) void k_tile(const uint16_t* __restrict__ X
         }
 }
 
+
+// ---------------------------------------------------------------------------
+// k_dma (v_mfma_f32_32x32x16_bf16).  Tiles of X and W go from HBM straight
+// into an S-stage LDS ring through buffer loads that write LDS (no register
+// staging), S - 1 stages ahead of the MFMAs, so the prefetch distance is
+// bounded by LDS capacity rather than by registers.  W stays as stored
+// ([k][n], n contiguous): ds_read_b64_tr_b16 gives each lane four
+// consecutive k of one column, and two such reads make an MFMA B operand.
+// X fragments are plain 16-byte LDS reads.  Both tiles are XOR-swizzled in
+// 16-byte groups -- a load's lanes fetch the global groups that the
+// permutation places at their LDS slots -- so fragment reads hit distinct
+// banks.  K must be a multiple of BK.
+//
+// ds_read_b64_tr_b16, per group of 16 lanes: lane i receives element i % 4
+// of the 8-byte segments addressed by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.
+// Pointing lane s at row kb + s/4, columns nb + 4 (s % 4) .. +3 of the W tile
+// gives lane i the four values W[kb .. kb+3][nb + i].
+template <int BM_, int BN_, int BK_, int NWM_, int NWN_, int S_>
+struct DmaCfg {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, NWM = NWM_, NWN = NWN_, S = S_;
+    static constexpr int NW = NWM * NWN, NT = NW * kWave;
+    static constexpr int WM = BM / NWM, WN = BN / NWN;
+    static constexpr int FM = WM / 32, FN = WN / 32;
+    static constexpr int XBYTES = BM * BK * 2, WBYTES = BK * BN * 2;
+    static constexpr int XI = XBYTES / 1024, WI = WBYTES / 1024;  // 1 KB loads per stage
+    static constexpr int TI = XI + WI;
+    static constexpr int LMAX = (TI + NW - 1) / NW, LMIN = TI / NW;  // loads per wave
+    static constexpr int XG = BK / 8, WG = BN / 8;                    // 16-byte groups per row
+    static constexpr int XROWS = 1024 / (BK * 2), WROWS = 1024 / (BN * 2);  // rows per load
+    static constexpr size_t LDS = (size_t)S * (XBYTES + WBYTES);
+    static_assert(BK == 32 || BK == 64, "X swizzle covers 4 or 8 groups per row");
+    static_assert(BN == 64 || BN == 128 || BN == 256 || BN == 512, "whole W rows per load");
+    static_assert(XBYTES % 1024 == 0, "whole X rows per load");
+    static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % NWM == 0 && BN % NWN == 0, "wave tile");
+    static_assert(S >= 3 && S <= 5 && (S - 2) * LMIN < 64, "ring depth / vmcnt range");
+};
+
+// Physical 16-byte group of logical group g in X row r (BK = 32: 4 groups of
+// 64-byte rows; BK = 64: 8 groups of 128-byte rows), and in W row kr.
+template <int XG>
+__device__ __forceinline__ int x_group(int g, int r) {
+    return XG == 4 ? (g ^ ((r >> 2) & 3)) : (g ^ ((r >> 1) & 7));
+}
+__device__ __forceinline__ int w_group_tr(int g, int kr) { return g ^ (2 * (kr & 3)); }
+
+// The LDS ring: one object per slot, so the compiler can tell that reads of
+// one slot never alias the loads filling another (and waits for neither).
+constexpr int kSlotBytes = 32768;
+constexpr int kMaxSlots = 5;
+__shared__ __align__(16) char g_slot0[kSlotBytes];
+__shared__ __align__(16) char g_slot1[kSlotBytes];
+__shared__ __align__(16) char g_slot2[kSlotBytes];
+__shared__ __align__(16) char g_slot3[kSlotBytes];
+__shared__ __align__(16) char g_slot4[kSlotBytes];
+template <typename Cfg, int D>
+__device__ __forceinline__ char* ring_slot() {
+    static_assert(Cfg::XBYTES + Cfg::WBYTES <= kSlotBytes && D < kMaxSlots, "ring slot");
+    if constexpr (D == 0) return g_slot0;
+    else if constexpr (D == 1) return g_slot1;
+    else if constexpr (D == 2) return g_slot2;
+    else if constexpr (D == 3) return g_slot3;
+    else return g_slot4;
+}
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_tr16(const char* p) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (s16x4_t __attribute__((address_space(3)))*)(p)));
+}
+
+// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt untouched): at most N of this wave's
+// vector memory operations still outstanding, no LDS/scalar ones.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+template <typename Cfg>
+struct DmaAddr {
+    const char* src[Cfg::LMAX];  // per-lane source of each load at stage 0
+    int64_t step[Cfg::LMAX];     // bytes a stage advances it by (uniform)
+};
+
+// Global -> LDS loads of the stage at k0 into slot D: lane l of load j writes
+// bytes [1024 j + 16 l, + 16) of the slot.  Lanes whose row or column lies
+// outside the matrix read the matrix's first bytes instead; their products
+// only reach outputs that are never stored.
+// 16 bytes per lane from global memory into LDS at (M0 + 16 lane).  Issued
+// as inline assembly: the compiler neither tracks these loads nor inserts
+// waits for them, so every wait on them is explicit (wait_vm_lgkm).
+__device__ __forceinline__ void lds_dma16(const char* src, uint32_t lds_base) {
+    // M0 holds the LDS base of the load; no code of this file keeps a value in
+    // M0 across this statement.
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
+}
+template <typename Cfg, int D>
+__device__ __forceinline__ uint32_t slot_lds_addr() {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ring_slot<Cfg, D>();
+}
+
+template <typename Cfg, int D>
+__device__ __forceinline__ void dma_issue(const DmaAddr<Cfg>& A, int wave, int64_t kstage) {
+    const uint32_t slot = slot_lds_addr<Cfg, D>();
+#pragma unroll
+    for (int i = 0; i < Cfg::LMAX; ++i) {
+        const int j = wave + i * Cfg::NW;
+        if (Cfg::TI % Cfg::NW != 0 && j >= Cfg::TI) continue;
+        lds_dma16(A.src[i] + kstage * A.step[i], __builtin_amdgcn_readfirstlane(slot + 1024 * j));
+    }
+}
+
+template <typename Cfg, int D>
+__device__ __forceinline__ void dma_compute(const uint32_t (&aoff)[Cfg::BK / 16], const uint32_t (&boff)[Cfg::FN],
+                                            f32x16_t (&acc)[Cfg::FM][Cfg::FN]) {
+    const char* xs = ring_slot<Cfg, D>();
+    const char* ws = xs + Cfg::XBYTES;
+#pragma unroll
+    for (int k16 = 0; k16 < Cfg::BK / 16; ++k16) {
+        uint4 a[Cfg::FM], b[Cfg::FN];
+#pragma unroll
+        for (int fm = 0; fm < Cfg::FM; ++fm)
+            a[fm] = *reinterpret_cast<const uint4*>(xs + aoff[k16] + fm * 32 * Cfg::BK * 2);
+#pragma unroll
+        for (int fn = 0; fn < Cfg::FN; ++fn) {
+            const char* p = ws + boff[fn] + k16 * 16 * Cfg::BN * 2;
+            const uint2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * Cfg::BN * 2);
+            b[fn] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+#pragma unroll
+        for (int fm = 0; fm < Cfg::FM; ++fm)
+#pragma unroll
+            for (int fn = 0; fn < Cfg::FN; ++fn) acc[fm][fn] = mfma32(a[fm], b[fn], acc[fm][fn]);
+    }
+}
+
+// One pipeline step: stage st from slot D; stage st + S - 1 into slot D - 1.
+template <typename Cfg, int D>
+__device__ __forceinline__ void dma_step(const DmaAddr<Cfg>& A, int wave, int64_t st, int64_t st1,
+                                         const uint32_t (&aoff)[Cfg::BK / 16],
+                                         const uint32_t (&boff)[Cfg::FN], f32x16_t (&acc)[Cfg::FM][Cfg::FN]) {
+    if (st >= st1) return;
+    // this wave's loads of stage st are done once at most those of the
+    // stages issued after it are outstanding; the barrier then publishes
+    // every wave's part of the slot
+    if (st + Cfg::S - 2 < st1) wait_vm_lgkm<(Cfg::S - 2) * Cfg::LMIN>();
+    else wait_vm_lgkm<0>();
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    if (st + Cfg::S - 1 < st1) dma_issue<Cfg, (D + Cfg::S - 1) % Cfg::S>(A, wave, st + Cfg::S - 1);
+    dma_compute<Cfg, D>(aoff, boff, acc);
+}
+
+template <typename Cfg, int... Ds>
+__device__ __forceinline__ void dma_round(const DmaAddr<Cfg>& A, int wave, int64_t base, int64_t st1,
+                                          const uint32_t (&aoff)[Cfg::BK / 16],
+                                          const uint32_t (&boff)[Cfg::FN], f32x16_t (&acc)[Cfg::FM][Cfg::FN],
+                                          std::integer_sequence<int, Ds...>) {
+    (dma_step<Cfg, Ds>(A, wave, base + Ds, st1, aoff, boff, acc), ...);
+}
+template <typename Cfg, int... Ds>
+__device__ __forceinline__ void dma_prologue(const DmaAddr<Cfg>& A, int wave, int64_t st0, int64_t st1,
+                                             std::integer_sequence<int, Ds...>) {
+    ((st0 + Ds < st1 ? dma_issue<Cfg, Ds>(A, wave, st0 + Ds) : void()), ...);
+}
+
+template <typename Cfg>
+__global__ __launch_bounds__(Cfg::NT) void k_dma(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+                                                 void* __restrict__ Y, int y_bf16, int64_t M, int64_t N,
+                                                 int64_t K, int splits, float* __restrict__ partial) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    // wave-uniform, so the loads' LDS base (M0) and their branches stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / Cfg::NWN, wn = wave % Cfg::NWN;
+    const int64_t m0 = (int64_t)blockIdx.x * Cfg::BM;
+    const int64_t n0 = (int64_t)blockIdx.y * Cfg::BN;
+    const int split = blockIdx.z;
+    const int64_t nst = (K + Cfg::BK - 1) / Cfg::BK;
+    const int64_t st0 = split * nst / splits, st1 = (split + 1) * nst / splits;
+
+    // K is a multiple of BK here: every stage lies inside the matrices
+    DmaAddr<Cfg> A;
+#pragma unroll
+    for (int i = 0; i < Cfg::LMAX; ++i) {
+        const int j = wave + i * Cfg::NW;
+        A.src[i] = reinterpret_cast<const char*>(X);
+        A.step[i] = 0;
+        if (j < Cfg::XI) {
+            const int r = j * Cfg::XROWS + lane / Cfg::XG;
+            const int g = x_group<Cfg::XG>(lane % Cfg::XG, r);
+            const int64_t m = m0 + r;
+            A.step[i] = Cfg::BK * 2;
+            if (m < M) A.src[i] = reinterpret_cast<const char*>(X + m * K + 8 * g);
+        } else if (j < Cfg::TI) {
+            const int kr = (j - Cfg::XI) * Cfg::WROWS + lane / Cfg::WG;
+            const int g = w_group_tr(lane % Cfg::WG, kr);
+            const int64_t n = n0 + 8 * g;
+            A.src[i] = reinterpret_cast<const char*>(W);
+            A.step[i] = (int64_t)Cfg::BK * N * 2;
+            if (n < N) A.src[i] = reinterpret_cast<const char*>(W + kr * N + n);
+        }
+    }
+    // fragment offsets within a slot
+    uint32_t aoff[Cfg::BK / 16], boff[Cfg::FN];
+    {
+        const int r = wm * Cfg::WM + (lane & 31);
+#pragma unroll
+        for (int k16 = 0; k16 < Cfg::BK / 16; ++k16)
+            aoff[k16] = (uint32_t)(r * Cfg::BK * 2 + 16 * x_group<Cfg::XG>(2 * k16 + (lane >> 5), r));
+        const int s = lane & 15;
+        const int kr = 8 * (lane >> 5) + (s >> 2);  // k16 = 0, h = 0
+#pragma unroll
+        for (int fn = 0; fn < Cfg::FN; ++fn) {
+            const int n = wn * Cfg::WN + 32 * fn + 16 * ((lane >> 4) & 1) + 4 * (s & 3);
+            boff[fn] = (uint32_t)(kr * Cfg::BN * 2 + 16 * w_group_tr(n >> 3, kr) + 2 * (n & 7));
+        }
+    }
+
+    f32x16_t acc[Cfg::FM][Cfg::FN];
+#pragma unroll
+    for (int a = 0; a < Cfg::FM; ++a)
+#pragma unroll
+        for (int b = 0; b < Cfg::FN; ++b)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[a][b][j] = 0.f;
+
+    dma_prologue<Cfg>(A, wave, st0, st1, std::make_integer_sequence<int, Cfg::S - 1>{});
+    for (int64_t base = st0; base < st1; base += Cfg::S)
+        dma_round<Cfg>(A, wave, base, st1, aoff, boff, acc, std::make_integer_sequence<int, Cfg::S>{});
+
+    const int l32 = lane & 31, g = lane >> 5;
+    float* dstp = splits > 1 ? partial + (int64_t)split * M * N : nullptr;
+#pragma unroll
+    for (int fm = 0; fm < Cfg::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < Cfg::FN; ++fn) {
+            const int64_t n = n0 + wn * Cfg::WN + 32 * fn + l32;
+            if (n >= N) continue;
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int64_t m = m0 + wm * Cfg::WM + 32 * fm + 8 * (j / 4) + 4 * g + (j % 4);
+                if (m >= M) continue;
+                const float v = acc[fm][fn][j];
+                if (dstp) dstp[m * N + n] = v;
+                else if (y_bf16) static_cast<uint16_t*>(Y)[m * N + n] = f32_to_bf16(v);
+                else static_cast<float*>(Y)[m * N + n] = v;
+            }
+        }
+}
+
 // Sum of split-K partials in split order.
 __global__ void k_reduce(const float* __restrict__ partial, void* __restrict__ Y, int y_bf16,
                          int64_t MN, int splits) {
@@ -449,11 +703,15 @@ __global__ void k_reduce(const float* __restrict__ partial, void* __restrict__ Y
 
 // ---- plans ---------------------------------------------------------------------
 // Per-M choices, measured on MI355X for K = 4096 and N = 14336 / 151936.
-using TileS = TileCfg<128, 128, 64, 32, 64>;   // 8 waves, M in (32, 256]
-using TileL = TileCfg<192, 256, 64, 96, 64>;   // 8 waves, M in (128, 192] with a wide N
-using TileB = TileCfg<256, 128, 64, 64, 64>;   // 8 waves, M > 256
+using TileS = TileCfg<128, 128, 64, 32, 64>;   // 8 waves; K not a multiple of 32
+using TileL = TileCfg<192, 256, 64, 96, 64>;
+using TileB = TileCfg<256, 128, 64, 64, 64>;
+using DmaS = DmaCfg<128, 128, 64, 2, 4, 4>;   // M in (32, 128], or (128, 256] on narrow N
+using DmaL = DmaCfg<192, 256, 32, 2, 4, 5>;   // M in (128, 192] on a wide N (lm-head)
+using DmaB = DmaCfg<256, 128, 32, 4, 2, 5>;   // M in (256, 768]
+using DmaH = DmaCfg<256, 256, 32, 2, 4, 4>;   // M > 768
 
-enum Kern { kStrip1, kStrip2, kTileS, kTileL, kTileB };
+enum Kern { kStrip1, kStrip2, kTileS, kTileL, kTileB, kDmaS, kDmaL, kDmaB, kDmaH };
 
 struct Plan {
     Kern kern;
@@ -474,12 +732,22 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
         return p;
     }
     int BM, BN, BK;
-    if (M > 128 && M <= 192 && (N + TileL::BN - 1) / TileL::BN >= cus) {
-        p.kern = kTileL; BM = TileL::BM; BN = TileL::BN; BK = TileL::BK;
+    auto pick = [&](Kern k, int bm, int bn, int bk) { p.kern = k; BM = bm; BN = bn; BK = bk; };
+    if (K % 64 == 0 && M <= 128) {
+        pick(kDmaS, DmaS::BM, DmaS::BN, DmaS::BK);
+    } else if (K % 32 == 0 && M <= 192 && (N + DmaL::BN - 1) / DmaL::BN >= cus) {
+        pick(kDmaL, DmaL::BM, DmaL::BN, DmaL::BK);
+    } else if (K % 64 == 0 && M <= 256) {
+        pick(kDmaS, DmaS::BM, DmaS::BN, DmaS::BK);
+    } else if (K % 32 == 0 && M > 256) {
+        if (M <= 768) pick(kDmaB, DmaB::BM, DmaB::BN, DmaB::BK);
+        else pick(kDmaH, DmaH::BM, DmaH::BN, DmaH::BK);
+    } else if (M > 128 && M <= 192 && (N + TileL::BN - 1) / TileL::BN >= cus) {
+        pick(kTileL, TileL::BM, TileL::BN, TileL::BK);
     } else if (M <= 256) {
-        p.kern = kTileS; BM = TileS::BM; BN = TileS::BN; BK = TileS::BK;
+        pick(kTileS, TileS::BM, TileS::BN, TileS::BK);
     } else {
-        p.kern = kTileB; BM = TileB::BM; BN = TileB::BN; BK = TileB::BK;
+        pick(kTileB, TileB::BM, TileB::BN, TileB::BK);
     }
     p.mtiles = (M + BM - 1) / BM;
     p.ntiles = (N + BN - 1) / BN;
@@ -498,6 +766,15 @@ int device_cus() {
     return cus > 0 ? cus : 256;
 }
 
+int launch_reduce(const Plan& p, float* partial, void* Y, int yb, int64_t M, int64_t N, hipStream_t s) {
+    if (p.splits <= 1) return SPEC_OK;
+    const int64_t MN = M * N;
+    const int64_t nthr = MN / 4;
+    hipLaunchKernelGGL(k_reduce, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s, partial, Y, yb, MN,
+                       p.splits);
+    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}
+
 template <typename Cfg, int D>
 int launch_tile(const Plan& p, const uint16_t* x, const uint16_t* w, void* Y, int yb, int64_t M,
                 int64_t N, int64_t K, float* partial, hipStream_t s) {
@@ -510,14 +787,16 @@ int launch_tile(const Plan& p, const uint16_t* x, const uint16_t* w, void* Y, in
     hipLaunchKernelGGL((k_tile<Cfg, D>), dim3((unsigned)p.mtiles, (unsigned)p.ntiles, (unsigned)p.splits),
                        dim3(Cfg::NT), lds, s, x, w, Y, yb, M, N, K, p.splits, partial);
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-    if (p.splits > 1) {
-        const int64_t MN = M * N;
-        const int64_t nthr = MN / 4;
-        hipLaunchKernelGGL(k_reduce, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s, partial,
-                           Y, yb, MN, p.splits);
-        if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-    }
-    return SPEC_OK;
+    return launch_reduce(p, partial, Y, yb, M, N, s);
+}
+
+template <typename Cfg>
+int launch_dma(const Plan& p, const uint16_t* x, const uint16_t* w, void* Y, int yb, int64_t M, int64_t N,
+               int64_t K, float* partial, hipStream_t s) {
+    hipLaunchKernelGGL((k_dma<Cfg>), dim3((unsigned)p.mtiles, (unsigned)p.ntiles, (unsigned)p.splits),
+                       dim3(Cfg::NT), 0, s, x, w, Y, yb, M, N, K, p.splits, partial);
+    if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+    return launch_reduce(p, partial, Y, yb, M, N, s);
 }
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
@@ -556,6 +835,10 @@ extern "C" int spec_verify_linear(const void* X, const void* W, void* Y, int y_d
         case kTileS: return launch_tile<TileS, 2>(p, x, w, Y, yb, M, N, Kd, partial, s);
         case kTileL: return launch_tile<TileL, 2>(p, x, w, Y, yb, M, N, Kd, partial, s);
         case kTileB: return launch_tile<TileB, 2>(p, x, w, Y, yb, M, N, Kd, partial, s);
+        case kDmaS: return launch_dma<DmaS>(p, x, w, Y, yb, M, N, Kd, partial, s);
+        case kDmaL: return launch_dma<DmaL>(p, x, w, Y, yb, M, N, Kd, partial, s);
+        case kDmaB: return launch_dma<DmaB>(p, x, w, Y, yb, M, N, Kd, partial, s);
+        case kDmaH: return launch_dma<DmaH>(p, x, w, Y, yb, M, N, Kd, partial, s);
     }
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
     return SPEC_OK;
