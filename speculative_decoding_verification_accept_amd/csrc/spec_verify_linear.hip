@@ -606,17 +606,21 @@ __device__ __forceinline__ void dma_prologue(const DmaAddr<Cfg>& A, int wave, in
     ((st0 + Ds < st1 ? dma_issue<Cfg, Ds>(A, wave, st0 + Ds) : void()), ...);
 }
 
+// Grid (m-tiles, n-tiles of this launch, K splits); n-tile ntile0 + blockIdx.y.
+// With splits > 1, the fp32 partial of split z goes to
+// partial[(z M + m) NP + n - ntile0 BN].
 template <typename Cfg>
 __global__ __launch_bounds__(Cfg::NT) void k_dma(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                                                  void* __restrict__ Y, int y_bf16, int64_t M, int64_t N,
-                                                 int64_t K, int splits, float* __restrict__ partial) {
+                                                 int64_t K, int splits, float* __restrict__ partial,
+                                                 int64_t ntile0, int64_t NP) {
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     // wave-uniform, so the loads' LDS base (M0) and their branches stay scalar
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = wave / Cfg::NWN, wn = wave % Cfg::NWN;
     const int64_t m0 = (int64_t)blockIdx.x * Cfg::BM;
-    const int64_t n0 = (int64_t)blockIdx.y * Cfg::BN;
+    const int64_t n0 = ((int64_t)blockIdx.y + ntile0) * Cfg::BN;
     const int split = blockIdx.z;
     const int64_t nst = (K + Cfg::BK - 1) / Cfg::BK;
     const int64_t st0 = split * nst / splits, st1 = (split + 1) * nst / splits;
@@ -672,7 +676,8 @@ __global__ __launch_bounds__(Cfg::NT) void k_dma(const uint16_t* __restrict__ X,
         dma_round<Cfg>(A, wave, base, st1, aoff, boff, acc, std::make_integer_sequence<int, Cfg::S>{});
 
     const int l32 = lane & 31, g = lane >> 5;
-    float* dstp = splits > 1 ? partial + (int64_t)split * M * N : nullptr;
+    const int64_t nbase = ntile0 * Cfg::BN;
+    float* dstp = splits > 1 ? partial + (int64_t)split * M * NP : nullptr;
 #pragma unroll
     for (int fm = 0; fm < Cfg::FM; ++fm)
 #pragma unroll
@@ -684,21 +689,24 @@ __global__ __launch_bounds__(Cfg::NT) void k_dma(const uint16_t* __restrict__ X,
                 const int64_t m = m0 + wm * Cfg::WM + 32 * fm + 8 * (j / 4) + 4 * g + (j % 4);
                 if (m >= M) continue;
                 const float v = acc[fm][fn][j];
-                if (dstp) dstp[m * N + n] = v;
+                if (dstp) dstp[m * NP + n - nbase] = v;
                 else if (y_bf16) static_cast<uint16_t*>(Y)[m * N + n] = f32_to_bf16(v);
                 else static_cast<float*>(Y)[m * N + n] = v;
             }
         }
 }
 
-// Sum of split-K partials in split order.
-__global__ void k_reduce(const float* __restrict__ partial, void* __restrict__ Y, int y_bf16,
-                         int64_t MN, int splits) {
-    const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-    if (i >= MN) return;  // MN % 4 == 0 (N % 8 == 0)
-    f32x4_t s = *reinterpret_cast<const f32x4_t*>(partial + i);
-    for (int sp = 1; sp < splits; ++sp) s += *reinterpret_cast<const f32x4_t*>(partial + sp * MN + i);
-    store_out(Y, y_bf16, i, s);
+// Sum of split-K partials in split order: partial [splits][M][NP] holds
+// columns nstart .. nstart + NP - 1 of Y; columns past N are skipped.
+__global__ void k_reduce(const float* __restrict__ partial, void* __restrict__ Y, int y_bf16, int64_t M,
+                         int64_t N, int64_t nstart, int64_t NP, int splits) {
+    const int64_t q = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;  // NP % 4 == 0
+    if (q >= M * NP) return;
+    const int64_t m = q / NP, c = q % NP;
+    if (nstart + c >= N) return;  // N % 8 == 0: all four columns are in range
+    f32x4_t s = *reinterpret_cast<const f32x4_t*>(partial + q);
+    for (int sp = 1; sp < splits; ++sp) s += *reinterpret_cast<const f32x4_t*>(partial + sp * M * NP + q);
+    store_out(Y, y_bf16, m * N + nstart + c, s);
 }
 
 // ---- plans ---------------------------------------------------------------------
@@ -713,10 +721,17 @@ using DmaH = DmaCfg<256, 256, 32, 2, 4, 4>;   // M > 768
 
 enum Kern { kStrip1, kStrip2, kTileS, kTileL, kTileB, kDmaS, kDmaL, kDmaB, kDmaH };
 
+// One or two launches over ranges of n-tiles; each may split K.
+struct Launch {
+    int64_t t0, t1;  // n-tiles [t0, t1)
+    int splits;
+};
 struct Plan {
     Kern kern;
     int64_t mtiles, ntiles;
-    int splits;
+    int BN;
+    Launch l[2];
+    int nl;
     size_t ws_bytes;
 };
 
@@ -727,8 +742,8 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
         const int mt = M <= 16 ? 1 : 2;
         p.mtiles = (M + 16 * mt - 1) / (16 * mt);
         p.ntiles = (N + kStripN - 1) / kStripN;
-        p.splits = 1;
-        p.ws_bytes = 0;
+        p.nl = 1;
+        p.l[0] = Launch{0, p.ntiles, 1};
         return p;
     }
     int BM, BN, BK;
@@ -749,13 +764,29 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
     } else {
         pick(kTileB, TileB::BM, TileB::BN, TileB::BK);
     }
+    p.BN = BN;
     p.mtiles = (M + BM - 1) / BM;
     p.ntiles = (N + BN - 1) / BN;
     const int64_t tiles = p.mtiles * p.ntiles;
     const int64_t nst = (K + BK - 1) / BK;
+    const bool dma = p.kern == kDmaS || p.kern == kDmaL || p.kern == kDmaB || p.kern == kDmaH;
+    const int64_t rem = p.ntiles % cus;
+    if (dma && p.mtiles == 1 && p.ntiles > cus && rem > 0 && 2 * rem <= cus && nst >= 16) {
+        // whole rounds of tiles, then the remainder split along K so that
+        // the last round keeps every compute unit streaming
+        int s2 = (int)(cus / rem);
+        s2 = s2 > 4 ? 4 : s2;
+        p.nl = 2;
+        p.l[0] = Launch{0, p.ntiles - rem, 1};
+        p.l[1] = Launch{p.ntiles - rem, p.ntiles, s2};
+        p.ws_bytes = align_up((size_t)s2 * M * rem * BN * sizeof(float), 256);
+        return p;
+    }
     // split K in two when the tiles alone leave more than half the machine idle
-    p.splits = (2 * tiles <= cus && nst >= 8) ? 2 : 1;
-    p.ws_bytes = p.splits > 1 ? align_up((size_t)p.splits * M * N * sizeof(float), 256) : 0;
+    const int sp = (2 * tiles <= cus && nst >= 8) ? 2 : 1;
+    p.nl = 1;
+    p.l[0] = Launch{0, p.ntiles, sp};
+    p.ws_bytes = sp > 1 ? align_up((size_t)sp * M * p.ntiles * BN * sizeof(float), 256) : 0;
     return p;
 }
 
@@ -766,12 +797,13 @@ int device_cus() {
     return cus > 0 ? cus : 256;
 }
 
-int launch_reduce(const Plan& p, float* partial, void* Y, int yb, int64_t M, int64_t N, hipStream_t s) {
-    if (p.splits <= 1) return SPEC_OK;
-    const int64_t MN = M * N;
-    const int64_t nthr = MN / 4;
-    hipLaunchKernelGGL(k_reduce, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s, partial, Y, yb, MN,
-                       p.splits);
+// NP: row stride of the partials, covering columns l.t0 BN .. l.t0 BN + NP - 1.
+int launch_reduce(const Launch& l, int BN, int64_t NP, float* partial, void* Y, int yb, int64_t M,
+                  int64_t N, hipStream_t s) {
+    if (l.splits <= 1) return SPEC_OK;
+    const int64_t nthr = M * NP / 4;
+    hipLaunchKernelGGL(k_reduce, dim3((unsigned)((nthr + 255) / 256)), dim3(256), 0, s, partial, Y, yb, M, N,
+                       l.t0 * BN, NP, l.splits);
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }
 
@@ -784,19 +816,26 @@ int launch_tile(const Plan& p, const uint16_t* x, const uint16_t* w, void* Y, in
                                 (int)lds) != hipSuccess)
             return SPEC_ERR_HIP;
     }
-    hipLaunchKernelGGL((k_tile<Cfg, D>), dim3((unsigned)p.mtiles, (unsigned)p.ntiles, (unsigned)p.splits),
-                       dim3(Cfg::NT), lds, s, x, w, Y, yb, M, N, K, p.splits, partial);
+    const Launch& l = p.l[0];  // k_tile plans have one launch over every tile
+    hipLaunchKernelGGL((k_tile<Cfg, D>), dim3((unsigned)p.mtiles, (unsigned)p.ntiles, (unsigned)l.splits),
+                       dim3(Cfg::NT), lds, s, x, w, Y, yb, M, N, K, l.splits, partial);
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-    return launch_reduce(p, partial, Y, yb, M, N, s);
+    return launch_reduce(l, Cfg::BN, N, partial, Y, yb, M, N, s);  // k_tile partials: row stride N
 }
 
 template <typename Cfg>
 int launch_dma(const Plan& p, const uint16_t* x, const uint16_t* w, void* Y, int yb, int64_t M, int64_t N,
                int64_t K, float* partial, hipStream_t s) {
-    hipLaunchKernelGGL((k_dma<Cfg>), dim3((unsigned)p.mtiles, (unsigned)p.ntiles, (unsigned)p.splits),
-                       dim3(Cfg::NT), 0, s, x, w, Y, yb, M, N, K, p.splits, partial);
-    if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-    return launch_reduce(p, partial, Y, yb, M, N, s);
+    for (int i = 0; i < p.nl; ++i) {
+        const Launch& l = p.l[i];
+        const int64_t NP = (l.t1 - l.t0) * Cfg::BN;
+        hipLaunchKernelGGL((k_dma<Cfg>), dim3((unsigned)p.mtiles, (unsigned)(l.t1 - l.t0), (unsigned)l.splits),
+                           dim3(Cfg::NT), 0, s, x, w, Y, yb, M, N, K, l.splits, partial, l.t0, NP);
+        if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+        const int rc = launch_reduce(l, Cfg::BN, NP, partial, Y, yb, M, N, s);
+        if (rc != SPEC_OK) return rc;
+    }
+    return SPEC_OK;
 }
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
