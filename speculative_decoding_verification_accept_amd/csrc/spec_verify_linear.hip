@@ -473,7 +473,8 @@ struct DmaCfg {
     static_assert(BN == 64 || BN == 128 || BN == 256 || BN == 512, "whole W rows per load");
     static_assert(XBYTES % 1024 == 0, "whole X rows per load");
     static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % NWM == 0 && BN % NWN == 0, "wave tile");
-    static_assert(S >= 3 && S <= 5 && (S - 2) * LMIN < 64, "ring depth / vmcnt range");
+    static_assert(S >= 2 && (S - 2) * LMIN < 64, "ring depth / vmcnt range");
+    static_assert(LDS <= 160 * 1024, "LDS");
 };
 
 // Physical 16-byte group of logical group g in X row r (BK = 32: 4 groups of
@@ -484,23 +485,18 @@ __device__ __forceinline__ int x_group(int g, int r) {
 }
 __device__ __forceinline__ int w_group_tr(int g, int kr) { return g ^ (2 * (kr & 3)); }
 
-// The LDS ring: one object per slot, so the compiler can tell that reads of
-// one slot never alias the loads filling another (and waits for neither).
-constexpr int kSlotBytes = 32768;
-constexpr int kMaxSlots = 5;
-__shared__ __align__(16) char g_slot0[kSlotBytes];
-__shared__ __align__(16) char g_slot1[kSlotBytes];
-__shared__ __align__(16) char g_slot2[kSlotBytes];
-__shared__ __align__(16) char g_slot3[kSlotBytes];
-__shared__ __align__(16) char g_slot4[kSlotBytes];
+// The LDS ring of S stage slots.  The loads that fill it are opaque to the
+// compiler (inline assembly with a memory clobber), so it neither waits for
+// them nor reuses LDS values across them; every wait is explicit.
+template <typename Cfg>
+__device__ __forceinline__ char* ring_base() {
+    __shared__ __align__(16) char ring[Cfg::S * (Cfg::XBYTES + Cfg::WBYTES)];
+    return ring;
+}
 template <typename Cfg, int D>
 __device__ __forceinline__ char* ring_slot() {
-    static_assert(Cfg::XBYTES + Cfg::WBYTES <= kSlotBytes && D < kMaxSlots, "ring slot");
-    if constexpr (D == 0) return g_slot0;
-    else if constexpr (D == 1) return g_slot1;
-    else if constexpr (D == 2) return g_slot2;
-    else if constexpr (D == 3) return g_slot3;
-    else return g_slot4;
+    static_assert(D < Cfg::S, "ring slot");
+    return ring_base<Cfg>() + D * (Cfg::XBYTES + Cfg::WBYTES);
 }
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -556,23 +552,28 @@ __device__ __forceinline__ void dma_compute(const uint32_t (&aoff)[Cfg::BK / 16]
                                             f32x16_t (&acc)[Cfg::FM][Cfg::FN]) {
     const char* xs = ring_slot<Cfg, D>();
     const char* ws = xs + Cfg::XBYTES;
+    constexpr int NK = Cfg::BK / 16;
+    // every fragment of the stage is requested before the first MFMA (this
+    // measured faster than interleaving reads and MFMAs per k16 step)
+    uint4 a[NK][Cfg::FM], b[NK][Cfg::FN];
 #pragma unroll
-    for (int k16 = 0; k16 < Cfg::BK / 16; ++k16) {
-        uint4 a[Cfg::FM], b[Cfg::FN];
+    for (int k16 = 0; k16 < NK; ++k16) {
 #pragma unroll
         for (int fm = 0; fm < Cfg::FM; ++fm)
-            a[fm] = *reinterpret_cast<const uint4*>(xs + aoff[k16] + fm * 32 * Cfg::BK * 2);
+            a[k16][fm] = *reinterpret_cast<const uint4*>(xs + aoff[k16] + fm * 32 * Cfg::BK * 2);
 #pragma unroll
         for (int fn = 0; fn < Cfg::FN; ++fn) {
             const char* p = ws + boff[fn] + k16 * 16 * Cfg::BN * 2;
             const uint2 lo = lds_tr16(p), hi = lds_tr16(p + 4 * Cfg::BN * 2);
-            b[fn] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            b[k16][fn] = make_uint4(lo.x, lo.y, hi.x, hi.y);
         }
+    }
+#pragma unroll
+    for (int k16 = 0; k16 < NK; ++k16)
 #pragma unroll
         for (int fm = 0; fm < Cfg::FM; ++fm)
 #pragma unroll
-            for (int fn = 0; fn < Cfg::FN; ++fn) acc[fm][fn] = mfma32(a[fm], b[fn], acc[fm][fn]);
-    }
+            for (int fn = 0; fn < Cfg::FN; ++fn) acc[fm][fn] = mfma32(a[k16][fm], b[k16][fn], acc[fm][fn]);
 }
 
 // One pipeline step: stage st from slot D; stage st + S - 1 into slot D - 1.
@@ -583,7 +584,8 @@ __device__ __forceinline__ void dma_step(const DmaAddr<Cfg>& A, int wave, int64_
     if (st >= st1) return;
     // this wave's loads of stage st are done once at most those of the
     // stages issued after it are outstanding; the barrier then publishes
-    // every wave's part of the slot
+    // every wave's part of the slot (and ends every read of the slot
+    // refilled below, made in the previous step)
     if (st + Cfg::S - 2 < st1) wait_vm_lgkm<(Cfg::S - 2) * Cfg::LMIN>();
     else wait_vm_lgkm<0>();
     __builtin_amdgcn_sched_barrier(0);
@@ -606,9 +608,6 @@ __device__ __forceinline__ void dma_prologue(const DmaAddr<Cfg>& A, int wave, in
     ((st0 + Ds < st1 ? dma_issue<Cfg, Ds>(A, wave, st0 + Ds) : void()), ...);
 }
 
-// Grid (m-tiles, n-tiles of this launch, K splits); n-tile ntile0 + blockIdx.y.
-// With splits > 1, the fp32 partial of split z goes to
-// partial[(z M + m) NP + n - ntile0 BN].
 template <typename Cfg>
 __global__ __launch_bounds__(Cfg::NT) void k_dma(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                                                  void* __restrict__ Y, int y_bf16, int64_t M, int64_t N,
