@@ -27,6 +27,10 @@ import sys
 import time
 
 HBM_PEAK_GBS = 8000.0
+# HBM bytes per call from FETCH_SIZE/WRITE_SIZE counter runs, calibrated on a
+# plain copy; stamped with the digest of the kernel sources they describe
+TRAFFIC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                               "traffic_lmhead_gemm_and_accept.md")
 BF16_PEAK_TFLOPS = 2500.0
 
 
@@ -241,6 +245,9 @@ def main():
         print(json.dumps(bench_gemm_sweep(torch, sv, workloads)))
         return
 
+    from speculative_decoding_verification_accept_amd import traffic
+    counted = traffic.read_committed(TRAFFIC_SUMMARY)   # None once the kernels changed
+
     r = bench_step(torch, sv, workloads, args.steps, args.warmup)
     ms = r["ms_per_step"]
     value = r["positions"] / (ms * 1e-3)
@@ -264,7 +271,8 @@ def main():
                    "M": r["positions"], "parallelism": "single GPU"},
         "roofline": {"kernel": "spec_verify_linear (lm-head, M=192)", "bound": "hbm",
                      "achieved": round(gemm_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gemm_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gemm_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": counted["lmhead_bytes"] if counted else None,
                      "avg_launch_us": round(r["gemm_ms"] * 1e3, 2),
                      "algorithmic_bytes": r["gemm_bytes"],
                      "tflops": round(r["gemm_flops"] / (r["gemm_ms"] * 1e-3) * 1e-12, 1)},
@@ -273,6 +281,7 @@ def main():
     if not args.no_breakdown:
         acc = bench_accept_large(torch, sv, workloads)
         acc = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in acc.items()}
+        acc["traffic_bytes"] = counted["accept_bytes"] if counted else None
         line["breakdown"] = {"accept_at_scale": acc,
                              "gemm_sweep": bench_gemm_sweep(torch, sv, workloads)}
     if not args.no_cpu_baseline:
