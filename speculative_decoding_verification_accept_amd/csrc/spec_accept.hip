@@ -541,6 +541,23 @@ struct Shared {
     uint64_t w0, w1;
 };
 
+// sh.lastpos = max(sh.lastpos, base + the last thread of the workgroup with
+// `pos` set): one ballot per wave and one LDS word per wave (same-address LDS
+// atomics from every thread would serialise).  Ends with a barrier.
+__device__ __forceinline__ void last_positive(bool pos, int base, Shared& sh) {
+    const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
+    const uint64_t m = __ballot(pos);
+    if (lane == 0) sh.red_x[wv] = m ? wv * kWave + 63 - __clzll((long long)m) : -1;
+    __syncthreads();
+    if (t == 0) {
+        int l = -1;
+#pragma unroll
+        for (int k = 0; k < kWaves; ++k) l = max(l, sh.red_x[k]);
+        if (l >= 0) sh.lastpos = max(sh.lastpos, base + l);
+    }
+    __syncthreads();
+}
+
 template <typename T, bool VEC>
 __device__ void write_invalid_row(const Args& g, int64_t b, int status, int t) {
     for (int i = t; i <= g.K; i += kThreads) g.out_tokens[b * (g.K + 1) + i] = -1;
@@ -874,14 +891,11 @@ __global__ __launch_bounds__(kThreads) void k_accept(Args g) {
         sh.u.s.scan[t + 1] = incl;
         if (t == 0) sh.u.s.scan[0] = carry;
         __syncthreads();
-        if (wk > 0.0) {
-            atomicMax(&sh.lastpos, k);
-            if (incl > tp && sh.u.s.scan[t] <= tp) {  // unique: the scan is non-decreasing
-                sh.cstar = k;
-                sh.tp = tp - sh.u.s.scan[t];
-            }
+        if (wk > 0.0 && incl > tp && sh.u.s.scan[t] <= tp) {  // unique: the scan is non-decreasing
+            sh.cstar = k;
+            sh.tp = tp - sh.u.s.scan[t];
         }
-        __syncthreads();
+        last_positive(wk > 0.0, k0, sh);
         if (sh.cstar >= 0) break;
         carry += btot;
     }
@@ -908,14 +922,11 @@ __global__ __launch_bounds__(kThreads) void k_accept(Args g) {
     sh.u.s.scan[t + 1] = incl2;
     if (t == 0) sh.u.s.scan[0] = 0.0;
     __syncthreads();
-    if (ts > 0.0) {
-        atomicMax(&sh.lastpos, t);
-        if (incl2 > tp && sh.u.s.scan[t] <= tp) {
-            sh.cstar = t;
-            sh.tp = tp - sh.u.s.scan[t];
-        }
+    if (ts > 0.0 && incl2 > tp && sh.u.s.scan[t] <= tp) {
+        sh.cstar = t;
+        sh.tp = tp - sh.u.s.scan[t];
     }
-    __syncthreads();
+    last_positive(ts > 0.0, 0, sh);
     int tstar = sh.cstar;
     tp = sh.tp;
     if (tstar < 0) {
