@@ -14,13 +14,14 @@
 // 8 consecutive k per lane; X (K contiguous) is used as stored.  The MFMA
 // computes D = A B with A an X fragment and B a W fragment.
 //
-//  k_strip (M <= 32, memory-bound): one 512-thread workgroup per 64-column
+//  k_strip (M <= 16, or <= 32 when K is not a multiple of 64; memory-bound):
+//    one 512-thread workgroup per 64-column
 //    strip of W, all M rows, the full K.  Each of its 8 waves takes a slice
 //    of K, keeps 4 k-steps of W loads in flight, transposes each lane's 8x4
 //    block of W in registers (v_perm_b32) straight into
 //    v_mfma_f32_16x16x32_bf16 operands, and the waves' partial tiles are
 //    summed through LDS in a fixed order.  W streams from HBM exactly once.
-//  k_dma (M > 32, K a multiple of 32 or 64; v_mfma_f32_32x32x16_bf16): a
+//  k_dma (M > 16, K a multiple of 32 or 64; v_mfma_f32_32x32x16_bf16): a
 //    workgroup computes a BM x BN tile.  Tiles of X and W go from HBM
 //    straight into an LDS ring of 4-5 stages by loads that write LDS, so the
 //    prefetch distance costs no registers; W stays [k][n] in LDS and the
@@ -713,7 +714,7 @@ __global__ void k_reduce(const float* __restrict__ partial, void* __restrict__ Y
 using TileS = TileCfg<128, 128, 64, 32, 64>;   // 8 waves; K not a multiple of 32
 using TileL = TileCfg<192, 256, 64, 96, 64>;
 using TileB = TileCfg<256, 128, 64, 64, 64>;
-using DmaS = DmaCfg<128, 128, 64, 2, 4, 4>;   // M in (32, 128], or (128, 256] on narrow N
+using DmaS = DmaCfg<128, 128, 64, 2, 4, 4>;   // M in (16, 128], or (128, 256] on narrow N
 using DmaL = DmaCfg<192, 256, 32, 2, 4, 5>;   // M in (128, 192] on a wide N (lm-head)
 using DmaB = DmaCfg<256, 128, 32, 4, 2, 5>;   // M in (256, 768]
 using DmaH = DmaCfg<256, 256, 32, 2, 4, 4>;   // M > 768
@@ -736,7 +737,10 @@ struct Plan {
 
 Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
     Plan p{};
-    if (M <= 32) {
+    // the strip kernel for a few rows; from 17 rows the 128x128 tile (K a
+    // multiple of 64) measured faster on MI355X (31.4 vs 34.0 us at M = 32,
+    // N = 14336, K = 4096)
+    if (M <= 16 || (M <= 32 && K % 64 != 0)) {
         p.kern = M <= 16 ? kStrip1 : kStrip2;
         const int mt = M <= 16 ? 1 : 2;
         p.mtiles = (M + 16 * mt - 1) / (16 * mt);
