@@ -14,6 +14,11 @@ V=128256 bf16 with ragged draft lengths (rotating over 5 input sets, 1.8 GB,
 so the 256 MB Infinity Cache cannot hold them), and the verify GEMM over the
 M = B(1+D) sweep against W [4096, 14336] (rotating over 5 weight copies).
 
+Also reported: the draft-depth controller (``spec_adapt``: telemetry and the
+next depth per row, after each accept pass) at B=64 and B=4096, and the depth
+planner (``spec_plan_depth``) fed with the GEMM sweep measured in the same
+run, giving the best draft depth per batch size.
+
 Roofline: the dominant kernel of the step is the lm-head GEMM; its achieved
 bandwidth is its algorithmic bytes (2KN + 2MK + 4MN) over its average launch
 duration, timed with HIP events on the stream it runs on.
@@ -41,7 +46,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-breakdown", action="store_true", help="time the step only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "accept", "gemm"], default=None,
+    ap.add_argument("--only", choices=["step", "accept", "gemm", "adapt"], default=None,
                     help="run one part only (for profiling)")
     return ap.parse_args()
 
@@ -178,6 +183,66 @@ def bench_gemm_sweep(torch, sv, workloads, reps=40, ncopies=5):
                 sweep=res)
 
 
+def bench_control(torch, sv, sweep, reps=200):
+    """spec_adapt latency after an accept pass (the telemetry and the next
+    depth per row), and the planner over the measured sweep."""
+    dev = torch.device("cuda:0")
+    K = 7
+    out = {"adapt": []}
+    for B in (64, 4096):
+        g = torch.Generator(device=dev)
+        g.manual_seed(B)
+        L = torch.randint(1, K + 1, (B,), generator=g, device=dev, dtype=torch.int32)
+        a = (torch.rand(B, generator=g, device=dev) * (L + 1).float()).floor().to(torch.int32)
+        st, tel = sv.adapt_state(B, dev), sv.adapt_telemetry(dev)
+        nxt = torch.empty(B, dtype=torch.int32, device=dev)
+        kw = dict(K=K, k_min=1, k_max=K, window=8, policy=sv.ADAPT_SPEEDUP, draft_cost=0.05, out=nxt)
+        for _ in range(10):
+            sv.adapt(a, L, st, tel, **kw)
+        torch.cuda.synchronize()
+        # one launch is a few microseconds of GPU work, less than what the
+        # Python binding takes to submit it: time a captured graph of `reps`
+        # launches so that the host is out of the measurement
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(reps):
+                    sv.adapt(a, L, st, tel, **kw)
+        torch.cuda.current_stream().wait_stream(side)
+        graph.replay()
+        torch.cuda.synchronize()
+        t0, t1 = _events(torch, 2)
+        t0.record()
+        graph.replay()
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / reps
+        # per row: a_b and L_b read, the 48-byte record read and written, the
+        # next length written
+        byts = B * (4 + 4 + 48 + 48 + 4)
+        out["adapt"].append(dict(B=B, K=K, us_per_call=round(us, 2), bytes=byts,
+                                 timing=f"graph of {reps} launches", bound="latency (one small launch)"))
+    if not sweep:
+        return out
+    m = [r["M"] for r in sweep]
+    t = [r["us"] for r in sweep]
+    batches = [1, 2, 4, 8, 16, 32, 64, 128]
+    plans = {}
+    t0 = time.perf_counter()
+    for alpha in (0.5, 0.7, 0.9):
+        p = sv.plan_depth(m, t, batches, d_max=7, alpha=alpha, draft_cost=0.05)
+        plans[f"alpha={alpha}"] = {str(b): {"D": int(p.best_depth[i]),
+                                            "speedup": round(float(p.speedup[i, p.best_depth[i]]), 3)}
+                                   for i, b in enumerate(batches)}
+    host_us = (time.perf_counter() - t0) * 1e6 / 3
+    out["plan"] = {"curve": "measured verify GEMM sweep above (one 4096x14336 layer)",
+                   "draft_cost": 0.05, "d_max": 7, "best_depth_by_batch": plans,
+                   "host_us_per_call": round(host_us, 1)}
+    return out
+
+
 def cpu_baseline(torch, workloads, st, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the step: the fp64
     GEMM reference on a column slice of the lm-head (scaled to all columns)
@@ -244,6 +309,9 @@ def main():
     if args.only == "gemm":
         print(json.dumps(bench_gemm_sweep(torch, sv, workloads)))
         return
+    if args.only == "adapt":
+        print(json.dumps(bench_control(torch, sv, [])))
+        return
 
     from speculative_decoding_verification_accept_amd import traffic
     counted = traffic.read_committed(TRAFFIC_SUMMARY)   # None once the kernels changed
@@ -282,8 +350,9 @@ def main():
         acc = bench_accept_large(torch, sv, workloads)
         acc = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in acc.items()}
         acc["traffic_bytes"] = counted["accept_bytes"] if counted else None
-        line["breakdown"] = {"accept_at_scale": acc,
-                             "gemm_sweep": bench_gemm_sweep(torch, sv, workloads)}
+        sweep = bench_gemm_sweep(torch, sv, workloads)
+        line["breakdown"] = {"accept_at_scale": acc, "gemm_sweep": sweep,
+                             "control": bench_control(torch, sv, sweep["sweep"])}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, workloads, r["state"])
     print(json.dumps(line), flush=True)

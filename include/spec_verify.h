@@ -156,11 +156,114 @@ int spec_verify_linear(const void* X, const void* W, void* Y, int y_dtype,
                        int64_t M, int64_t N, int64_t Kd, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * spec_adapt -- acceptance telemetry and the adaptive draft depth, run on
+ * the GPU after a verify pass, from that pass's out_accepted.
+ *
+ * Defined by: page "Decode is memory-bound: ~59 tok/s ceiling on an RTX
+ * 4090, and how speculative decoding beats it" (trefon.com), section "Two
+ * things that follow from the math" (the adaptive mode caps the draft depth
+ * once the measured acceptance falls under 35%) and the closing rules (pick
+ * the depth from the measured acceptance, keep measuring); section
+ * "Speculative decoding" (E(a, k) = 1 + a + ... + a^k, speedup
+ * E / (k c + 1)).  Page "Speculative decoding and early exit ..."
+ * (reactapp.top), section "Production perspective" and the operational
+ * checklist (acceptance rate, mean accepted length, acceptance histograms).
+ *
+ * For each row b with a = accepted[b] and L = draft_lens[b] (K if NULL):
+ *   - a valid row (0 <= L <= K, 0 <= a <= L) ran a + 1 acceptance tests if
+ *     a < L, else a; if it ran any, (a, tests) enters the row's record, a
+ *     ring of its last 16 such passes.  Any other row (a = -1 from an
+ *     invalid accept row, or inconsistent values) is counted as invalid and
+ *     leaves its record unchanged.
+ *   - S, N = accepted drafts and tests over the record's last
+ *     min(window, recorded) passes; the measured acceptance is S / N.
+ *   - next_lens[b] = k_max if N == 0; otherwise
+ *       SPEC_ADAPT_THRESHOLD: k_min if S < accept_floor * N (fp64), else k_max;
+ *       SPEC_ADAPT_SPEEDUP:   the k in [k_min, k_max] maximising
+ *                             E(S/N, k) / (k * draft_cost + 1), lowest on ties
+ *                             (fp64, E summed term by term).
+ * Telemetry: the block of SPEC_ADAPT_TELEMETRY_WORDS uint64 counters is
+ * ADDED to (zero it once to start counting).  Word layout:
+ *   [0] valid rows  [1] invalid rows  [2] drafted (sum L)  [3] tests run
+ *   [4] accepted drafts (sum a)  [5] emitted tokens (sum a + 1)  [6] calls
+ *   [8 + i]   tests run at draft position i        (i < SPEC_ADAPT_MAX_K)
+ *   [40 + i]  drafts accepted at position i        (i < SPEC_ADAPT_MAX_K)
+ *   [72 + d]  rows given next depth d               (d <= SPEC_ADAPT_MAX_K)
+ *   [105 + L * 33 + a]  valid rows with draft length L and a accepted drafts
+ *   the rest reserved (left as they are).
+ *
+ * Arguments (device pointers, caller-owned):
+ *   accepted     [B] int32 (spec_accept's out_accepted)
+ *   draft_lens   [B] int32 or NULL (every row verified K drafts)
+ *   B            rows, 0 .. 2^31; K: the max draft length of that pass, 0..32
+ *   state        [B] records of SPEC_ADAPT_STATE_BYTES, 16-byte aligned;
+ *                zero = no history.  Bytes 0-15 the accepted counts of the
+ *                ring, 16-31 the test counts, 32-35 the passes recorded
+ *                (uint32; the ring slot of pass n is n mod 16), 36-39 the
+ *                last depth chosen (int32), 40-63 reserved.
+ *   telemetry    SPEC_ADAPT_TELEMETRY_WORDS uint64, 8-byte aligned
+ *   next_lens    [B] int32: the next pass's draft length per row
+ *   1 <= k_min <= k_max <= SPEC_ADAPT_MAX_K; 1 <= window <= 16
+ *   policy       SPEC_ADAPT_THRESHOLD or SPEC_ADAPT_SPEEDUP
+ *   accept_floor in [0, 1] (0.35 in the page's adaptive mode)
+ *   draft_cost   c >= 0, finite (used by SPEC_ADAPT_SPEEDUP)
+ * Errors: SPEC_ERR_INVALID_ARG (host validation, nothing enqueued),
+ * SPEC_ERR_HIP.  Calls that share a state or telemetry block must be
+ * ordered on one stream.
+ * ---------------------------------------------------------------------- */
+#define SPEC_ADAPT_MAX_K 32
+#define SPEC_ADAPT_STATE_BYTES 64
+#define SPEC_ADAPT_TELEMETRY_WORDS 1200
+#define SPEC_ADAPT_THRESHOLD 0
+#define SPEC_ADAPT_SPEEDUP 1
+
+size_t spec_adapt_state_bytes(int64_t B);
+size_t spec_adapt_telemetry_bytes(void);
+
+int spec_adapt(const int32_t* accepted, const int32_t* draft_lens, int64_t B, int K,
+               void* state, uint64_t* telemetry, int32_t* next_lens, int k_min, int k_max,
+               int window, int policy, double accept_floor, double draft_cost, void* stream);
+
+/* ------------------------------------------------------------------------
+ * spec_plan_depth -- HOST function: the draft depth per batch size from a
+ * measured verify-cost curve, and the throughput / interactivity frontier.
+ *
+ * Defined by: agentnet.co.il item on speculative decoding, section "The
+ * formula behind the speedup" (speculation pays when the verify time at
+ * B(1+D) rows over that at B rows is below the accepted length; the best D
+ * depends on B along a Pareto frontier of throughput against
+ * interactivity) and section "GEMM-M grows, a small batch suffices"
+ * (M = B(1+D)); page "Decode is memory-bound ..." (trefon.com), section
+ * "Speculative decoding" (E(a, D) and the draft cost c).
+ *
+ * With T(M) the measured pass time at M rows (linear between points, flat
+ * below the first, the last segment's slope above the last), for batch B
+ * and depth D in [0, d_max]:
+ *   den = T(B(1+D)) + (D c) T(B)
+ *   speedup[B, D] = (E(a, D) T(B)) / den
+ *   tokens_per_s[B, D] = (B E(a, D)) / den * 1e6   (t_pts in microseconds)
+ *   best_depth[B] = argmax_D speedup (lowest D on ties)
+ *   pareto[B, D] = 1 iff no other (B', D') has total tokens/s and
+ *                  per-sequence tokens/s (E / den) both >= and one >.
+ * Arguments (HOST pointers): m_pts [n_pts] int64 strictly ascending, >= 1;
+ * t_pts [n_pts] > 0 finite; batches [n_batches] in [1, 2^31]; d_max in
+ * [0, SPEC_MAX_DRAFT]; alpha in [0, 1]; draft_cost >= 0 finite;
+ * out_best_depth [n_batches] int32; out_speedup, out_tokens_per_s
+ * [n_batches, d_max+1] double, out_pareto [n_batches, d_max+1] uint8, each
+ * may be NULL.  Returns SPEC_OK or SPEC_ERR_INVALID_ARG.  Allocates host
+ * memory only.
+ * ---------------------------------------------------------------------- */
+int spec_plan_depth(const int64_t* m_pts, const double* t_pts, int n_pts,
+                    const int64_t* batches, int n_batches, int d_max, double alpha,
+                    double draft_cost, int32_t* out_best_depth, double* out_speedup,
+                    double* out_tokens_per_s, uint8_t* out_pareto);
+
 /* Human-readable text of a return code (static storage). */
 const char* spec_status_string(int code);
 
 /* ABI version of this header (incremented on incompatible changes). */
-#define SPEC_VERIFY_ABI_VERSION 1
+#define SPEC_VERIFY_ABI_VERSION 2
 int spec_abi_version(void);
 
 #ifdef __cplusplus

@@ -7,6 +7,9 @@ fallback -- if the library is missing, calls raise.
 
 * :func:`accept` -- batched accept/reject pass (``spec_accept``)
 * :func:`verify_linear` -- verify linear layer Y = X W (``spec_verify_linear``)
+* :func:`adapt` -- acceptance telemetry and next draft depth (``spec_adapt``)
+* :func:`plan_depth` -- draft depth per batch size from a measured verify-cost
+  curve (``spec_plan_depth``, a host function)
 """
 from __future__ import annotations
 
@@ -14,6 +17,7 @@ import ctypes
 import os
 from typing import NamedTuple
 
+import numpy as np
 import torch
 
 from . import _build
@@ -31,6 +35,11 @@ ROW_ZERO_Q = 8
 ROW_RESID_ZERO = 16
 ROW_STALLED = 32
 MAX_DRAFT = 255
+ADAPT_MAX_K = 32
+ADAPT_STATE_BYTES = 64
+ADAPT_TELEMETRY_WORDS = 1200
+ADAPT_THRESHOLD = 0
+ADAPT_SPEEDUP = 1
 
 # (name, restype, argtypes) for every entry point declared in the header
 _P = ctypes.c_void_p
@@ -44,6 +53,14 @@ ABI = [
     ("spec_verify_linear_workspace_bytes", ctypes.c_size_t, [_I64, _I64, _I64]),
     ("spec_verify_linear", ctypes.c_int,
      [_P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    ("spec_adapt_state_bytes", ctypes.c_size_t, [_I64]),
+    ("spec_adapt_telemetry_bytes", ctypes.c_size_t, []),
+    ("spec_adapt", ctypes.c_int,
+     [_P, _P, _I64, ctypes.c_int, _P, _P, _P, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+      ctypes.c_int, ctypes.c_double, ctypes.c_double, _P]),
+    ("spec_plan_depth", ctypes.c_int,
+     [_P, _P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+      _P, _P, _P, _P]),
     ("spec_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("spec_abi_version", ctypes.c_int, []),
 ]
@@ -207,3 +224,100 @@ def verify_linear(X, W, *, out=None, out_dtype=torch.float32, workspace=None, st
     if rc != SPEC_OK:
         raise SpecError("spec_verify_linear", rc)
     return out
+
+
+# --- controller ---------------------------------------------------------------
+
+# telemetry word offsets (the layout spec_adapt documents)
+TEL_ROWS, TEL_INVALID, TEL_DRAFTED, TEL_TESTED, TEL_ACCEPTED, TEL_EMITTED, TEL_CALLS = range(7)
+TEL_TESTED_AT = 8
+TEL_ACCEPTED_AT = TEL_TESTED_AT + ADAPT_MAX_K
+TEL_DEPTH_HIST = TEL_ACCEPTED_AT + ADAPT_MAX_K
+TEL_HIST = TEL_DEPTH_HIST + ADAPT_MAX_K + 1
+
+
+def adapt_state(B: int, device) -> torch.Tensor:
+    """Zeroed per-row controller records ([B, 64] bytes): no history yet."""
+    return torch.zeros(B, ADAPT_STATE_BYTES, dtype=torch.uint8, device=device)
+
+
+def adapt_telemetry(device) -> torch.Tensor:
+    """A zeroed telemetry block (int64 view of the uint64 counters)."""
+    return torch.zeros(ADAPT_TELEMETRY_WORDS, dtype=torch.int64, device=device)
+
+
+def adapt(accepted, draft_lens, state, telemetry, *, K: int, k_min: int = 1, k_max: int,
+          window: int = 8, policy: int = ADAPT_THRESHOLD, accept_floor: float = 0.35,
+          draft_cost: float = 0.0, out=None, stream=None) -> torch.Tensor:
+    """Acceptance telemetry and the next draft length per row (``spec_adapt``).
+
+    accepted [B] int32 (``accept(...).accepted``); draft_lens [B] int32 or
+    None (every row verified K drafts); state [B, 64] uint8 and telemetry
+    [1200] int64 are updated in place.  Returns next_lens [B] int32.
+    """
+    _check_dev("accepted", accepted, torch.int32, 1)
+    B = accepted.shape[0]
+    if draft_lens is not None:
+        _check_dev("draft_lens", draft_lens, torch.int32, 1)
+        if draft_lens.shape[0] != B:
+            raise ValueError("draft_lens must be [B]")
+    _check_dev("state", state, torch.uint8, 2)
+    if tuple(state.shape) != (B, ADAPT_STATE_BYTES):
+        raise ValueError("state must be [B, 64] uint8")
+    _check_dev("telemetry", telemetry, torch.int64, 1)
+    if telemetry.shape[0] != ADAPT_TELEMETRY_WORDS:
+        raise ValueError("telemetry must hold 1200 words")
+    if out is None:
+        out = torch.empty(B, dtype=torch.int32, device=accepted.device)
+    _check_dev("out", out, torch.int32, 1)
+    rc = load_library().spec_adapt(
+        _ptr(accepted), _ptr(draft_lens), B, K, _ptr(state), _ptr(telemetry), _ptr(out),
+        k_min, k_max, window, policy, float(accept_floor), float(draft_cost), _stream(stream))
+    if rc != SPEC_OK:
+        raise SpecError("spec_adapt", rc)
+    return out
+
+
+def telemetry_counters(telemetry) -> dict:
+    """The telemetry block's counters by name (host copy; no arithmetic)."""
+    t = telemetry.detach().cpu().numpy().astype(np.uint64)
+    k = ADAPT_MAX_K
+    return {
+        "rows": int(t[TEL_ROWS]), "invalid_rows": int(t[TEL_INVALID]),
+        "drafted": int(t[TEL_DRAFTED]), "tested": int(t[TEL_TESTED]),
+        "accepted": int(t[TEL_ACCEPTED]), "emitted": int(t[TEL_EMITTED]),
+        "calls": int(t[TEL_CALLS]),
+        "tested_at": t[TEL_TESTED_AT:TEL_TESTED_AT + k].astype(np.int64),
+        "accepted_at": t[TEL_ACCEPTED_AT:TEL_ACCEPTED_AT + k].astype(np.int64),
+        "depth_hist": t[TEL_DEPTH_HIST:TEL_DEPTH_HIST + k + 1].astype(np.int64),
+        "hist": t[TEL_HIST:TEL_HIST + (k + 1) ** 2].astype(np.int64).reshape(k + 1, k + 1),
+    }
+
+
+class DepthPlan(NamedTuple):
+    best_depth: np.ndarray     # [nB] int32
+    speedup: np.ndarray        # [nB, d_max+1]
+    tokens_per_s: np.ndarray   # [nB, d_max+1] (whole batch)
+    pareto: np.ndarray         # [nB, d_max+1] bool
+
+
+def plan_depth(m_pts, t_us, batches, *, d_max: int, alpha: float, draft_cost: float = 0.0) -> DepthPlan:
+    """Draft depth per batch size from a measured verify-cost curve
+    (``spec_plan_depth``, host code): m_pts rows (ascending) with their pass
+    times t_us in microseconds."""
+    m = np.ascontiguousarray(m_pts, dtype=np.int64)
+    t = np.ascontiguousarray(t_us, dtype=np.float64)
+    b = np.ascontiguousarray(batches, dtype=np.int64)
+    if m.shape != t.shape or m.ndim != 1:
+        raise ValueError("m_pts and t_us must be 1-D of equal length")
+    nb, nd = b.shape[0], d_max + 1
+    best = np.zeros(nb, np.int32)
+    sp = np.zeros((nb, nd))
+    rate = np.zeros((nb, nd))
+    par = np.zeros((nb, nd), np.uint8)
+    c = lambda a: a.ctypes.data_as(ctypes.c_void_p)
+    rc = load_library().spec_plan_depth(c(m), c(t), m.shape[0], c(b), nb, d_max, float(alpha),
+                                        float(draft_cost), c(best), c(sp), c(rate), c(par))
+    if rc != SPEC_OK:
+        raise SpecError("spec_plan_depth", rc)
+    return DepthPlan(best, sp, rate, par.astype(bool))

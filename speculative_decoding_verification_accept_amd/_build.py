@@ -4,7 +4,8 @@ Every HIP source is compiled with -O3 for gfx950 only.  Packed-fp32 VALU
 instructions are disabled (-packed-fp32-ops); the accept/reject kernels are
 compiled with -ffp-contract=off so that every fused multiply-add in them is
 written out explicitly and the weights recomputed in different kernels are
-bit-identical.
+bit-identical; so are the depth controller and planner, whose fp64
+expressions are evaluated exactly in the order written.
 """
 from __future__ import annotations
 
@@ -28,6 +29,8 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 PER_FILE = {
     "spec_accept.hip": ["-ffp-contract=off"],
     "spec_verify_linear.hip": [],
+    "spec_adapt.hip": ["-ffp-contract=off"],
+    "spec_plan.cpp": ["-ffp-contract=off"],
     "api.cpp": [],
 }
 

@@ -31,14 +31,15 @@ def test_header_declares_the_boundary():
     fns = _declared_functions()
     assert fns == sorted(["spec_accept", "spec_accept_workspace_bytes", "spec_verify_linear",
                           "spec_verify_linear_workspace_bytes", "spec_status_string",
-                          "spec_abi_version"]), fns
+                          "spec_abi_version", "spec_adapt", "spec_adapt_state_bytes",
+                          "spec_adapt_telemetry_bytes", "spec_plan_depth"]), fns
     assert sorted(n for n, _, _ in sv.ABI) == fns
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.spec_abi_version() == 1
+    assert lib.spec_abi_version() == 2
     assert sv.status_string(0) == "ok"
     assert "invalid" in sv.status_string(-1)
 
@@ -119,3 +120,50 @@ def test_python_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         sv.verify_linear(torch.zeros(2, 8, dtype=torch.bfloat16),
                          torch.zeros(8, 8, dtype=torch.bfloat16))
+
+
+def _adapt(lib, **kw):
+    a = dict(acc=FAKE, L=None, B=4, K=5, st=FAKE, tel=FAKE, nxt=FAKE, kmin=1, kmax=5, W=8,
+             pol=0, floor=0.35, c=0.0, s=None)
+    a.update(kw)
+    return lib.spec_adapt(a["acc"], a["L"], a["B"], a["K"], a["st"], a["tel"], a["nxt"],
+                          a["kmin"], a["kmax"], a["W"], a["pol"], a["floor"], a["c"], a["s"])
+
+
+def test_adapt_sizes_and_argument_validation(lib):
+    assert lib.spec_adapt_state_bytes(10) == 640
+    assert lib.spec_adapt_state_bytes(-1) == 0
+    assert lib.spec_adapt_telemetry_bytes() == 1200 * 8
+    E = sv.SPEC_ERR_INVALID_ARG
+    assert _adapt(lib, B=-1) == E
+    assert _adapt(lib, K=33) == E
+    assert _adapt(lib, K=-1) == E
+    assert _adapt(lib, kmin=0) == E
+    assert _adapt(lib, kmin=6, kmax=5) == E
+    assert _adapt(lib, kmax=33) == E
+    assert _adapt(lib, W=0) == E
+    assert _adapt(lib, W=17) == E
+    assert _adapt(lib, pol=2) == E
+    assert _adapt(lib, floor=1.5) == E
+    assert _adapt(lib, floor=float("nan")) == E
+    assert _adapt(lib, c=-0.1) == E
+    assert _adapt(lib, c=float("inf")) == E
+    assert _adapt(lib, tel=None) == E
+    assert _adapt(lib, tel=ctypes.c_void_p(0x100004)) == E
+    assert _adapt(lib, st=FAKE_ODD) == E
+    assert _adapt(lib, acc=None) == E
+    assert _adapt(lib, nxt=None) == E
+
+
+def test_plan_depth_argument_validation():
+    E = sv.SPEC_ERR_INVALID_ARG
+    ok = dict(m_pts=[1, 8, 64], t_us=[20.0, 21.0, 30.0], batches=[1, 4], d_max=7, alpha=0.7)
+    sv.plan_depth(**ok)
+    for bad in (dict(m_pts=[8, 1, 64]), dict(m_pts=[0, 8, 64]), dict(t_us=[20.0, -1.0, 30.0]),
+                dict(t_us=[20.0, float("nan"), 30.0]), dict(batches=[0, 4]), dict(d_max=-1),
+                dict(d_max=256), dict(alpha=1.01), dict(alpha=float("nan"))):
+        with pytest.raises(sv.SpecError) as ei:
+            sv.plan_depth(**{**ok, **bad})
+        assert ei.value.code == E, bad
+    with pytest.raises(sv.SpecError):
+        sv.plan_depth(**ok, draft_cost=-1.0)
