@@ -7,10 +7,16 @@
  *   spec_verify_linear  the verify linear layer, Y = X W, whose row count
  *                       grows from B to B(1+D) when D drafts are verified;
  *   spec_accept         the batched accept/reject pass over the target's
- *                       vocabulary distributions.
+ *                       vocabulary distributions;
+ * and the control around it:
+ *   spec_adapt          acceptance telemetry and the next draft depth per
+ *                       row, on the GPU, from spec_accept's output;
+ *   spec_plan_depth     (host) the draft depth per batch size from a
+ *                       measured verify-cost curve.
  *
  * Conventions shared by every entry point:
- *  - Tensor pointers are DEVICE pointers, allocated and owned by the caller.
+ *  - Tensor pointers are DEVICE pointers, allocated and owned by the caller
+ *    (spec_plan_depth alone takes host arrays).
  *    The library allocates nothing and keeps no state between calls, so
  *    calls on different streams may run concurrently provided their
  *    workspaces do not overlap.
