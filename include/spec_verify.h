@@ -9,6 +9,8 @@
  *   spec_accept         the batched accept/reject pass over the target's
  *                       vocabulary distributions;
  * and the control around it:
+ *   spec_verify_attention  the verify pass's attention: K+1 causal
+ *                       queries per sequence against its KV cache;
  *   spec_adapt          acceptance telemetry and the next draft depth per
  *                       row, on the GPU, from spec_accept's output;
  *   spec_plan_depth     (host) the draft depth per batch size from a
@@ -264,6 +266,56 @@ int spec_plan_depth(const int64_t* m_pts, const double* t_pts, int n_pts,
                     const int64_t* batches, int n_batches, int d_max, double alpha,
                     double draft_cost, int32_t* out_best_depth, double* out_speedup,
                     double* out_tokens_per_s, uint8_t* out_pareto);
+
+/* ------------------------------------------------------------------------
+ * spec_verify_attention -- attention of a verify pass: the K+1 query
+ * positions of each sequence against its KV cache, causal within the
+ * verified block, grouped KV heads.
+ *
+ * Defined by: page "Speculative decoding and early exit: accelerated
+ * autoregressive decoding" (reactapp.top), section "Attention structure
+ * during decoding" (each step's queries read the sequence's whole key/value
+ * memory; one head: Q [8, 1, 128] against K, V [8, 2048, 128]) and section
+ * "Speculative decoding: draft first, then verify" (one target pass over
+ * K+1 positions); page "Decode is memory-bound ..." (trefon.com), ceiling
+ * section (at long context the cache is read in full on every pass).
+ *
+ * For sequence b with ctx_b cached tokens and L_b drafts (draft_lens[b], K
+ * if NULL), query i = 0 .. L_b (the token that ended the previous pass,
+ * then the drafts) sits at position ctx_b + i; its key and value must
+ * already be in the cache there.  For query head h (KV head g = h / (H/Hkv)):
+ *   out[b, i, h, :] = sum_{j <= ctx_b + i} softmax_j(scale * q[b,i,h,:].k[b,g,j,:]) v[b,g,j,:]
+ * Rows i > L_b are written as zeros.  fp32 accumulation; the probabilities
+ * enter the value product rounded to bf16.
+ *
+ * Arguments (device pointers, caller-owned, 16-byte aligned):
+ *   q          [B, K+1, H, 128] bf16
+ *   k_cache, v_cache  [B, Hkv, S, 128] bf16 (S = cache capacity per sequence)
+ *   ctx_lens   [B] int32; draft_lens [B] int32 or NULL
+ *   B in [0, 65535]; K >= 0; H a multiple of Hkv; (K+1) * (H/Hkv) <= 32;
+ *   head_dim == 128; scale finite
+ *   out        [B, K+1, H, 128] of out_dtype (SPEC_F32 or SPEC_BF16)
+ *   out_status [B] int32 or NULL: SPEC_ROW_BAD_LEN when ctx_b < 0, L_b is
+ *              outside [0, K] or ctx_b + L_b + 1 > S (that row's output is
+ *              zero); 0 otherwise
+ *   workspace  spec_verify_attention_workspace_bytes(B, K, H, Hkv, S) bytes
+ *              (0 when the cache is not split across workgroups; may then be
+ *              NULL), contents need not be initialised
+ * The cache capacity S sets how the keys are split across workgroups:
+ * pass the batch's longest ctx_b + L_b + 1 rather than a much larger
+ * allocation size for the best split.
+ * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+#define SPEC_ATTN_HEAD_DIM 128
+#define SPEC_ATTN_MAX_ROWS 32
+
+size_t spec_verify_attention_workspace_bytes(int64_t B, int K, int H, int Hkv, int64_t S);
+
+int spec_verify_attention(const void* q, const void* k_cache, const void* v_cache,
+                          const int32_t* ctx_lens, const int32_t* draft_lens, int64_t B, int K,
+                          int H, int Hkv, int64_t S, int head_dim, float scale, void* out,
+                          int out_dtype, int32_t* out_status, void* workspace,
+                          size_t workspace_bytes, void* stream);
 
 /* Human-readable text of a return code (static storage). */
 const char* spec_status_string(int code);

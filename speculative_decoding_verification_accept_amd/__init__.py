@@ -7,6 +7,8 @@ fallback -- if the library is missing, calls raise.
 
 * :func:`accept` -- batched accept/reject pass (``spec_accept``)
 * :func:`verify_linear` -- verify linear layer Y = X W (``spec_verify_linear``)
+* :func:`verify_attention` -- the verify pass's attention, K+1 causal queries
+  per sequence against its KV cache (``spec_verify_attention``)
 * :func:`adapt` -- acceptance telemetry and next draft depth (``spec_adapt``)
 * :func:`plan_depth` -- draft depth per batch size from a measured verify-cost
   curve (``spec_plan_depth``, a host function)
@@ -53,6 +55,11 @@ ABI = [
     ("spec_verify_linear_workspace_bytes", ctypes.c_size_t, [_I64, _I64, _I64]),
     ("spec_verify_linear", ctypes.c_int,
      [_P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    ("spec_verify_attention_workspace_bytes", ctypes.c_size_t,
+     [_I64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _I64]),
+    ("spec_verify_attention", ctypes.c_int,
+     [_P, _P, _P, _P, _P, _I64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _I64, ctypes.c_int,
+      ctypes.c_float, _P, ctypes.c_int, _P, _P, ctypes.c_size_t, _P]),
     ("spec_adapt_state_bytes", ctypes.c_size_t, [_I64]),
     ("spec_adapt_telemetry_bytes", ctypes.c_size_t, []),
     ("spec_adapt", ctypes.c_int,
@@ -223,6 +230,62 @@ def verify_linear(X, W, *, out=None, out_dtype=torch.float32, workspace=None, st
                                 nbytes, _stream(stream))
     if rc != SPEC_OK:
         raise SpecError("spec_verify_linear", rc)
+    return out
+
+
+# --- verify attention ---------------------------------------------------------
+
+ATTN_HEAD_DIM = 128
+ATTN_MAX_ROWS = 32
+
+
+def attention_workspace_bytes(B: int, K: int, H: int, Hkv: int, S: int) -> int:
+    return int(load_library().spec_verify_attention_workspace_bytes(B, K, H, Hkv, S))
+
+
+def verify_attention(q, k_cache, v_cache, ctx_lens, draft_lens=None, *, scale=None, out=None,
+                     out_dtype=torch.float32, status=None, workspace=None, stream=None):
+    """Attention of a verify pass (``spec_verify_attention``).
+
+    q [B, K+1, H, 128] bf16; k_cache, v_cache [B, Hkv, S, 128] bf16;
+    ctx_lens [B] int32 (cached tokens before the pass); draft_lens [B] int32
+    or None.  Query i of sequence b attends to cache positions 0 .. ctx_b + i.
+    Returns out [B, K+1, H, 128] (rows past L_b are zero).
+    """
+    _check_dev("q", q, torch.bfloat16, 4)
+    _check_dev("k_cache", k_cache, torch.bfloat16, 4)
+    _check_dev("v_cache", v_cache, torch.bfloat16, 4)
+    B, K1, H, d = q.shape
+    _, Hkv, S, d2 = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape) or k_cache.shape[0] != B or d2 != d:
+        raise ValueError("k_cache and v_cache must be [B, Hkv, S, head_dim]")
+    _check_dev("ctx_lens", ctx_lens, torch.int32, 1)
+    if draft_lens is not None:
+        _check_dev("draft_lens", draft_lens, torch.int32, 1)
+    if out is None:
+        out = torch.empty(B, K1, H, d, dtype=out_dtype, device=q.device)
+    _check_dev("out", out, None, 4)
+    if out.dtype == torch.float32:
+        od = SPEC_F32
+    elif out.dtype == torch.bfloat16:
+        od = SPEC_BF16
+    else:
+        raise TypeError("out must be float32 or bfloat16")
+    if status is not None:
+        _check_dev("status", status, torch.int32, 1)
+    if scale is None:
+        scale = float(d) ** -0.5
+    lib = load_library()
+    need = lib.spec_verify_attention_workspace_bytes(B, K1 - 1, H, Hkv, S)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.spec_verify_attention(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(ctx_lens), _ptr(draft_lens), B, K1 - 1, H,
+        Hkv, S, d, float(scale), _ptr(out), od, _ptr(status), _ptr(workspace), nbytes,
+        _stream(stream))
+    if rc != SPEC_OK:
+        raise SpecError("spec_verify_attention", rc)
     return out
 
 

@@ -214,3 +214,27 @@ def large_accept_device(seed: int, device, B: int = 64, K: int = 7, V: int = 128
     z = (3.0 * torch.randn(B, K + 1, V, generator=g, device=device)).to(torch.bfloat16)
     q, x, L = draft_side_device(z, K, 1.5, 0.8, g, ragged=True)
     return z, q, x, L
+
+
+# --- verify attention ------------------------------------------------------------
+# Shapes: the pages' decode example is one head of Q [8, 1, 128] against a
+# 2048-token cache, 32 heads (multi-head); the grouped variant uses 8 KV heads
+# for 32 query heads, head dim 128, the attention of the model whose linear
+# layer is the 4096 x 14336 sweep.
+ATTN_HEAD_DIM = 128
+
+
+def attention_inputs(B: int, K: int, H: int, Hkv: int, ctx_lens, S: int, seed: int, device,
+                     draft_lens=None):
+    """bf16 q [B, K+1, H, 128] and caches [B, Hkv, S, 128] ~ N(0, 1), drawn
+    with torch's seeded generator on `device`; positions past each
+    sequence's ctx_b + L_b + 1 hold the same draws (never read)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    q = torch.randn(B, K + 1, H, ATTN_HEAD_DIM, generator=g, device=device).to(torch.bfloat16)
+    kc = torch.randn(B, Hkv, S, ATTN_HEAD_DIM, generator=g, device=device).to(torch.bfloat16)
+    vc = torch.randn(B, Hkv, S, ATTN_HEAD_DIM, generator=g, device=device).to(torch.bfloat16)
+    ctx = torch.as_tensor(np.asarray(ctx_lens, dtype=np.int32), device=device)
+    lens = None if draft_lens is None else torch.as_tensor(np.asarray(draft_lens, dtype=np.int32),
+                                                           device=device)
+    return q, kc, vc, ctx, lens

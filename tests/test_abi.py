@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     assert fns == sorted(["spec_accept", "spec_accept_workspace_bytes", "spec_verify_linear",
                           "spec_verify_linear_workspace_bytes", "spec_status_string",
                           "spec_abi_version", "spec_adapt", "spec_adapt_state_bytes",
-                          "spec_adapt_telemetry_bytes", "spec_plan_depth"]), fns
+                          "spec_adapt_telemetry_bytes", "spec_plan_depth",
+                          "spec_verify_attention", "spec_verify_attention_workspace_bytes"]), fns
     assert sorted(n for n, _, _ in sv.ABI) == fns
 
 
@@ -167,3 +168,38 @@ def test_plan_depth_argument_validation():
         assert ei.value.code == E, bad
     with pytest.raises(sv.SpecError):
         sv.plan_depth(**ok, draft_cost=-1.0)
+
+
+def _attn(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ctx=FAKE, L=None, B=2, K=3, H=8, Hkv=2, S=4096, d=128,
+             sc=0.088, out=FAKE, od=0, st=None, ws=FAKE, wsb=1 << 30, s=None)
+    a.update(kw)
+    return lib.spec_verify_attention(a["q"], a["k"], a["v"], a["ctx"], a["L"], a["B"], a["K"],
+                                     a["H"], a["Hkv"], a["S"], a["d"], a["sc"], a["out"], a["od"],
+                                     a["st"], a["ws"], a["wsb"], a["s"])
+
+
+def test_attention_argument_validation(lib):
+    E = sv.SPEC_ERR_INVALID_ARG
+    assert _attn(lib, d=64) == E                 # head dim 128 only
+    assert _attn(lib, H=6, Hkv=4) == E           # H not a multiple of Hkv
+    assert _attn(lib, K=8, H=8, Hkv=2) == E      # (K+1) * 4 = 36 rows > 32
+    assert _attn(lib, K=-1) == E
+    assert _attn(lib, B=-1) == E
+    assert _attn(lib, B=70000) == E
+    assert _attn(lib, S=0) == E
+    assert _attn(lib, od=3) == E
+    assert _attn(lib, sc=float("nan")) == E
+    assert _attn(lib, sc=float("inf")) == E
+    assert _attn(lib, q=None) == E
+    assert _attn(lib, ctx=None) == E
+    assert _attn(lib, out=None) == E
+    assert _attn(lib, q=FAKE_ODD) == E
+    assert _attn(lib, ws=None) == sv.SPEC_ERR_WORKSPACE   # split cache needs partials
+    assert _attn(lib, wsb=64) == sv.SPEC_ERR_WORKSPACE
+    assert _attn(lib, B=0) == sv.SPEC_OK
+    # many sequences fill the machine without splitting: no workspace
+    assert lib.spec_verify_attention_workspace_bytes(256, 3, 32, 8, 4096) == 0
+    n = lib.spec_verify_attention_workspace_bytes(1, 7, 32, 8, 32768)
+    assert n >= 8 * 2 * 32 * 128 * 4
+    assert lib.spec_verify_attention_workspace_bytes(1, 8, 8, 2, 64) == 0   # invalid shape
