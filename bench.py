@@ -14,7 +14,11 @@ V=128256 bf16 with ragged draft lengths (rotating over 5 input sets, 1.8 GB,
 so the 256 MB Infinity Cache cannot hold them), and the verify GEMM over the
 M = B(1+D) sweep against W [4096, 14336] (rotating over 5 weight copies).
 
-Also reported: the draft-depth controller (``spec_adapt``: telemetry and the
+Also reported: verify attention (``spec_verify_attention``: the K+1 queries
+of each sequence against its KV cache) at D = 0, 3, 7 on the pages' decode
+example (8 sequences x 2048 tokens, 32 heads of 128) and on grouped-head
+shapes (32 query / 8 KV heads), against the HBM roofline of the cache bytes;
+the draft-depth controller (``spec_adapt``: telemetry and the
 next depth per row, after each accept pass) at B=64 and B=4096, and the depth
 planner (``spec_plan_depth``) fed with the GEMM sweep measured in the same
 run, giving the best draft depth per batch size.
@@ -46,7 +50,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-breakdown", action="store_true", help="time the step only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "accept", "gemm", "adapt"], default=None,
+    ap.add_argument("--only", choices=["step", "accept", "gemm", "adapt", "attn"], default=None,
                     help="run one part only (for profiling)")
     return ap.parse_args()
 
@@ -183,6 +187,54 @@ def bench_gemm_sweep(torch, sv, workloads, reps=40, ncopies=5):
                 sweep=res)
 
 
+def bench_attention(torch, sv, workloads, reps=30):
+    """Verify attention per call at D = 0, 3, 7: the cache is read once per
+    call whatever D is, so the time should stay flat in D while the rows
+    grow (1+D)-fold."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+    cases = [("decode example, multi-head", 8, 32, 32, 2048, 1),
+             ("grouped heads", 8, 32, 8, 8192, 1),
+             ("grouped heads, 32 sequences", 32, 32, 8, 4096, 1),
+             ("grouped heads, one long sequence", 1, 32, 8, 32768, 2)]
+    res = []
+    for label, B, H, Hkv, ctx_len, nsets in cases:
+        row = {"case": label, "B": B, "H": H, "Hkv": Hkv, "ctx": ctx_len, "by_D": []}
+        for D in (0, 3, 7):
+            S = ctx_len + D + 1
+            ctx = [ctx_len] * B
+            sets = [workloads.attention_inputs(B, D, H, Hkv, ctx, S, seed=100 * D + k, device=dev)
+                    for k in range(nsets)]
+            out = torch.empty(B, D + 1, H, 128, dtype=torch.bfloat16, device=dev)
+            need = sv.attention_workspace_bytes(B, D, H, Hkv, S)
+            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            for k in range(nsets):
+                q, kc, vc, ct, _ = sets[k]
+                sv.verify_attention(q, kc, vc, ct, out=out, workspace=ws)
+            torch.cuda.synchronize()
+            t0, t1 = _events(torch, 2)
+            t0.record()
+            for r in range(reps):
+                q, kc, vc, ct, _ = sets[r % nsets]
+                sv.verify_attention(q, kc, vc, ct, out=out, workspace=ws)
+            t1.record()
+            torch.cuda.synchronize()
+            us = t0.elapsed_time(t1) * 1e3 / reps
+            kv = B * (ctx_len + D + 1) * Hkv * 128 * 2 * 2
+            qo = 2 * B * (D + 1) * H * 128 * 2
+            gbs = (kv + qo) / us * 1e-3
+            row["by_D"].append(dict(D=D, rows_per_kv_head=(D + 1) * (H // Hkv), us=round(us, 2),
+                                    bytes=kv + qo, GBs=round(gbs, 1),
+                                    frac_hbm=round(gbs / HBM_PEAK_GBS, 3)))
+            del sets, out, ws
+        t = [r["us"] for r in row["by_D"]]
+        row["time_D7_over_D0"] = round(t[2] / t[0], 3)
+        res.append(row)
+    return dict(workload="spec_verify_attention: q [B, D+1, H, 128] bf16 against k/v caches "
+                         "[B, Hkv, ctx+D+1, 128] bf16, N(0,1), scale 1/sqrt(128), bf16 out",
+                cases=res)
+
+
 def bench_control(torch, sv, sweep, reps=200):
     """spec_adapt latency after an accept pass (the telemetry and the next
     depth per row), and the planner over the measured sweep."""
@@ -309,6 +361,9 @@ def main():
     if args.only == "gemm":
         print(json.dumps(bench_gemm_sweep(torch, sv, workloads)))
         return
+    if args.only == "attn":
+        print(json.dumps(bench_attention(torch, sv, workloads)))
+        return
     if args.only == "adapt":
         print(json.dumps(bench_control(torch, sv, [])))
         return
@@ -352,6 +407,7 @@ def main():
         acc["traffic_bytes"] = counted["accept_bytes"] if counted else None
         sweep = bench_gemm_sweep(torch, sv, workloads)
         line["breakdown"] = {"accept_at_scale": acc, "gemm_sweep": sweep,
+                             "verify_attention": bench_attention(torch, sv, workloads),
                              "control": bench_control(torch, sv, sweep["sweep"])}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, workloads, r["state"])

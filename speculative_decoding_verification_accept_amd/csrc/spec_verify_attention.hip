@@ -37,7 +37,7 @@
 // last row (a cache hit) instead of branching around the loads.
 // The four waves' states merge in LDS (log-sum-exp); with one split the
 // workgroup writes the normalised output, else an unnormalised partial that
-// k_attn_combine merges over the splits in a fixed order.
+// k_attn_combine merges over the splits (a fixed grouping and order).
 #include "spec_verify.h"
 #include "device_common.hpp"
 
@@ -158,35 +158,41 @@ __device__ __forceinline__ void attend_step(const Stage& st, int64_t kb, int64_t
         float mx = sv[0];
 #pragma unroll
         for (int j = 1; j < 8; ++j) mx = fmaxf(mx, sv[j]);
-        mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-        const float mnew = fmaxf(ws.m[rt], mx);
-        const float alpha = mnew == -INFINITY ? 1.f : hw_exp2(ws.m[rt] - mnew);
-        ws.m[rt] = mnew;
+        // The running max of a row moves only when one of its scores exceeds
+        // it; otherwise every rescale factor is exactly 1 (2^0), so the
+        // cross-lane max and the rescale of the outputs are skipped for the
+        // whole wave (same results, bit for bit).
+        if (__ballot(mx > ws.m[rt])) {
+            mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+            mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+            const float mnew = fmaxf(ws.m[rt], mx);
+            const float alpha = mnew == -INFINITY ? 1.f : hw_exp2(ws.m[rt] - mnew);
+            ws.m[rt] = mnew;
+            ws.l[rt] *= alpha;
+            // rows of the output tile held by this lane: 4 kg + r; their
+            // factor lives in lane 4 kg + r (query row = lane % 16)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float ar = __shfl(alpha, 4 * kg + r, kWave);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ws.o[rt][e][r] *= ar;
+            }
+        }
+        const float mnew = ws.m[rt];
         float p[8], ps = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             p[j] = sv[j] == -INFINITY ? 0.f : hw_exp2(sv[j] - mnew);
             ps += p[j];
         }
-        ws.l[rt] = ws.l[rt] * alpha + ps;
-        // rows of the output tile held by this lane: 4 kg + r; their factor
-        // lives in lane 4 kg + r (query row = lane % 16)
-        float ar[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * kg + r, kWave);
+        ws.l[rt] += ps;
         uint4 pa;
         pa.x = (uint32_t)f32_to_bf16(p[0]) | ((uint32_t)f32_to_bf16(p[1]) << 16);
         pa.y = (uint32_t)f32_to_bf16(p[2]) | ((uint32_t)f32_to_bf16(p[3]) << 16);
         pa.z = (uint32_t)f32_to_bf16(p[4]) | ((uint32_t)f32_to_bf16(p[5]) << 16);
         pa.w = (uint32_t)f32_to_bf16(p[6]) | ((uint32_t)f32_to_bf16(p[7]) << 16);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            f32x4_t o = ws.o[rt][e];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] *= ar[r];
-            ws.o[rt][e] = mfma16(pa, bv[e], o);
-        }
+        for (int e = 0; e < 8; ++e) ws.o[rt][e] = mfma16(pa, bv[e], ws.o[rt][e]);
     }
 }
 
@@ -294,27 +300,65 @@ __global__ __launch_bounds__(kAThreads) void k_attn(AttnArgs a) {
     if (direct && a.status && s == 0 && g == 0 && t == 0) a.status[b] = L < 0 ? SPEC_ROW_BAD_LEN : 0;
 }
 
-// One workgroup per (query row r, KV head g, sequence b); thread = head dim.
-__global__ __launch_bounds__(kD) void k_attn_combine(AttnArgs a) {
-    const int dim = threadIdx.x, r = blockIdx.x, g = blockIdx.y;
+// One workgroup per (query row r, KV head g, sequence b): ng groups of 128
+// threads (thread = head dim; ng = blockDim / 128, at most 4, just enough
+// that one batch covers the splits when it can) take the splits
+// s = group (mod ng), eight at a time with every load issued before use,
+// each keeping a running (max, sum, output); the groups then merge in LDS in
+// group order.
+constexpr int kCGroups = 4;
+constexpr int kCBatch = 8;
+
+__global__ __launch_bounds__(kCGroups * kD) void k_attn_combine(AttnArgs a) {
+    __shared__ float cm[kCGroups], cl[kCGroups], co[kCGroups][kD];
+    const int dim = threadIdx.x % kD, grp = threadIdx.x / kD, ng = blockDim.x / kD;
+    const int r = blockIdx.x, g = blockIdx.y;
     const int64_t b = blockIdx.z;
     int ctx, T;
     const int L = seq_len(a, b, ctx, T);
     const int64_t base = (b * a.Hkv + g) * a.nsplit * a.R + r;  // split s at base + s R
-    float M = -INFINITY;
-    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[2 * (base + (int64_t)s * a.R)]);
-    float o = 0.f, ls = 0.f;
+    float m = -INFINITY, l = 0.f, o = 0.f;
+    for (int s0 = grp; s0 < a.nsplit; s0 += ng * kCBatch) {
+        float ms[kCBatch], ls[kCBatch], os[kCBatch];
+#pragma unroll
+        for (int k = 0; k < kCBatch; ++k) {
+            const int s = s0 + k * ng;
+            const int64_t pr = base + (int64_t)min(s, a.nsplit - 1) * a.R;
+            ms[k] = a.part_ml[2 * pr];
+            ls[k] = a.part_ml[2 * pr + 1];
+            os[k] = a.part_o[pr * kD + dim];
+            if (s >= a.nsplit) ms[k] = -INFINITY;
+        }
+#pragma unroll
+        for (int k = 0; k < kCBatch; ++k) {
+            const float mn = fmaxf(m, ms[k]);
+            if (mn == -INFINITY) continue;
+            const float fa = m == -INFINITY ? 0.f : hw_exp2(m - mn);
+            const float fb = ms[k] == -INFINITY ? 0.f : hw_exp2(ms[k] - mn);
+            o = o * fa + os[k] * fb;
+            l = l * fa + ls[k] * fb;
+            m = mn;
+        }
+    }
+    co[grp][dim] = o;
+    if (dim == 0) {
+        cm[grp] = m;
+        cl[grp] = l;
+    }
+    __syncthreads();
+    if (grp != 0) return;
+    float M = cm[0];
+    for (int k = 1; k < ng; ++k) M = fmaxf(M, cm[k]);
+    float ot = 0.f, lt = 0.f;
     if (M != -INFINITY) {
-        for (int s = 0; s < a.nsplit; ++s) {
-            const int64_t pr = base + (int64_t)s * a.R;
-            const float ms = a.part_ml[2 * pr];
-            const float f = ms == -INFINITY ? 0.f : hw_exp2(ms - M);
-            o += a.part_o[pr * kD + dim] * f;
-            ls += a.part_ml[2 * pr + 1] * f;
+        for (int k = 0; k < ng; ++k) {
+            const float f = cm[k] == -INFINITY ? 0.f : hw_exp2(cm[k] - M);
+            ot += co[k][dim] * f;
+            lt += cl[k] * f;
         }
     }
     const int i = r / a.G, h = g * a.G + r % a.G;
-    const float v = (i <= L && ls > 0.f) ? o / ls : 0.f;
+    const float v = (i <= L && lt > 0.f) ? ot / lt : 0.f;
     store_val(a.out, a.out_bf16, ((b * (a.K + 1) + i) * a.H + h) * kD + dim, v);
     if (a.status && r == 0 && g == 0 && dim == 0) a.status[b] = L < 0 ? SPEC_ROW_BAD_LEN : 0;
 }
@@ -331,7 +375,7 @@ AttnPlan attn_plan(int64_t B, int K, int H, int Hkv, int64_t S) {
     ns = std::min<int64_t>(ns, std::max<int64_t>((S + kSplitMinKeys - 1) / kSplitMinKeys, 1));
     ns = std::max<int64_t>(ns, 1);
     int64_t chunk = (S + ns - 1) / ns;
-    chunk = (chunk + kRound - 1) / kRound * kRound;
+    chunk = (chunk + kStep - 1) / kStep * kStep;
     ns = (S + chunk - 1) / chunk;
     p.nsplit = (int)ns;
     p.chunk = (int)chunk;
@@ -404,7 +448,9 @@ extern "C" int spec_verify_attention(const void* q, const void* k_cache, const v
     else hipLaunchKernelGGL(k_attn<2>, grid, dim3(kAThreads), 0, st, a);
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
     if (p.nsplit > 1) {
-        hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)a.R, (unsigned)Hkv, (unsigned)B), dim3(kD), 0, st, a);
+        const int ng = std::min(kCGroups, (p.nsplit + kCBatch - 1) / kCBatch);
+        hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)a.R, (unsigned)Hkv, (unsigned)B),
+                           dim3(ng * kD), 0, st, a);
         if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
     }
     return SPEC_OK;
