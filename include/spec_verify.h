@@ -7,7 +7,9 @@
  *   spec_verify_linear  the verify linear layer, Y = X W, whose row count
  *                       grows from B to B(1+D) when D drafts are verified;
  *   spec_accept         the batched accept/reject pass over the target's
- *                       vocabulary distributions;
+ *                       vocabulary distributions (spec_accept_sampled: the
+ *                       same with the draft as logits and the sampler's
+ *                       top-p / min-p filters on both distributions);
  * and the control around it:
  *   spec_verify_attention  the verify pass's attention: K+1 causal
  *                       queries per sequence against its KV cache;
@@ -60,6 +62,8 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 #define SPEC_ROW_ZERO_Q 8      /* q_i(x_i) not > 0 at a position < L_b (stochastic mode) */
 #define SPEC_ROW_RESID_ZERO 16 /* informational: the residual max(p - q, 0) summed to 0,
                                   the token was drawn from p instead */
+#define SPEC_ROW_FILTER_COARSE 64 /* informational (spec_accept_sampled): a top-p cut fell in
+                                  a bin of more than 4096 entries, which was kept whole */
 #define SPEC_ROW_STALLED 32    /* the row's workgroups did not all make progress within the
                                   wait bound (about 0.1 s); out_accepted[b] = -1, the rest
                                   of the row's outputs are unspecified, and the workspace
@@ -135,6 +139,49 @@ int spec_accept(const void* target_logits, int logits_dtype,
                 uint64_t philox_offset, int32_t* out_tokens, int32_t* out_accepted,
                 float* out_p_draft, int32_t* out_status, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * spec_accept_sampled -- accept/reject with the production sampler's
+ * filters; the draft is given as logits.
+ *
+ * Defined by: page "Decode is memory-bound: ~59 tok/s ceiling on an RTX
+ * 4090, and how speculative decoding beats it" (trefon.com), section "Two
+ * things that follow from the math" (production sampler: temperature 0.6,
+ * top-p 0.95, min-p 0.05; the draft sampler matched to the target's) and
+ * section "Speculative decoding" (acceptance rule, exactness); page
+ * "Speculative decoding and early exit ..." (reactapp.top), listing
+ * speculative_decode (q is the tempered softmax of the draft's logits).
+ *
+ * For each row, as spec_accept, with p and q replaced by the filtered
+ * distributions p' = F(softmax(target_logits[b,i,:] / temperature)) and
+ * q' = F(softmax(draft_logits[b,i,:] / draft_temperature)), where F keeps
+ * token j iff (a) the probability of the tokens with a strictly larger logit
+ * sums to less than top_p and (b) p_j >= min_p * max_k p_k, and renormalises
+ * the kept mass.  top_p == 1 and min_p == 0 turn (a) and (b) off.  A draft
+ * token outside q''s kept set makes the row invalid (SPEC_ROW_ZERO_Q).
+ * out_p_draft holds p'_i(x_i).  Same uniforms, inverse-CDF rule, residual
+ * fall-back and per-row status bits as spec_accept, plus the informational
+ * SPEC_ROW_FILTER_COARSE.
+ *
+ * Arguments: as spec_accept, except
+ *   draft_logits   [B, K, V] of logits_dtype (the same dtype as the target)
+ *   temperature, draft_temperature   finite, > 0 (no greedy mode here)
+ *   top_p in (0, 1]; min_p in [0, 1)
+ *   workspace      spec_accept_sampled_workspace_bytes(B, K, V) bytes,
+ *                  16-byte aligned; its first 256 * B bytes must be ZERO when
+ *                  the call starts (every call leaves them zero)
+ * Two launches on `stream`: per-distribution statistics (max, top-p cut,
+ * kept mass), then the decisions and draws.
+ * ---------------------------------------------------------------------- */
+size_t spec_accept_sampled_workspace_bytes(int64_t B, int K, int64_t V);
+
+int spec_accept_sampled(const void* target_logits, const void* draft_logits, int logits_dtype,
+                        const int32_t* draft_tokens, const int32_t* draft_lens, int64_t B, int K,
+                        int64_t V, int64_t row_base, float temperature, float draft_temperature,
+                        float top_p, float min_p, uint64_t philox_seed, uint64_t philox_offset,
+                        int32_t* out_tokens, int32_t* out_accepted, float* out_p_draft,
+                        int32_t* out_status, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /* ------------------------------------------------------------------------
  * spec_verify_linear -- Y[M, N] = X[M, Kd] W[Kd, N], bf16 operands, fp32

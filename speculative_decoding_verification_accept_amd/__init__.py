@@ -6,6 +6,8 @@ of the computation runs in the library's HIP kernels, and there is no CPU
 fallback -- if the library is missing, calls raise.
 
 * :func:`accept` -- batched accept/reject pass (``spec_accept``)
+* :func:`accept_sampled` -- the same with the draft as logits and the
+  sampler's top-p / min-p filters (``spec_accept_sampled``)
 * :func:`verify_linear` -- verify linear layer Y = X W (``spec_verify_linear``)
 * :func:`verify_attention` -- the verify pass's attention, K+1 causal queries
   per sequence against its KV cache (``spec_verify_attention``)
@@ -36,6 +38,7 @@ ROW_BAD_LEN = 4
 ROW_ZERO_Q = 8
 ROW_RESID_ZERO = 16
 ROW_STALLED = 32
+ROW_FILTER_COARSE = 64
 MAX_DRAFT = 255
 ADAPT_MAX_K = 32
 ADAPT_STATE_BYTES = 64
@@ -52,6 +55,11 @@ ABI = [
     ("spec_accept", ctypes.c_int,
      [_P, ctypes.c_int, _P, _P, _P, _I64, ctypes.c_int, _I64, _I64, ctypes.c_float, _U64, _U64,
       _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("spec_accept_sampled_workspace_bytes", ctypes.c_size_t, [_I64, ctypes.c_int, _I64]),
+    ("spec_accept_sampled", ctypes.c_int,
+     [_P, _P, ctypes.c_int, _P, _P, _I64, ctypes.c_int, _I64, _I64, ctypes.c_float,
+      ctypes.c_float, ctypes.c_float, ctypes.c_float, _U64, _U64, _P, _P, _P, _P, _P,
+      ctypes.c_size_t, _P]),
     ("spec_verify_linear_workspace_bytes", ctypes.c_size_t, [_I64, _I64, _I64]),
     ("spec_verify_linear", ctypes.c_int,
      [_P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
@@ -197,6 +205,57 @@ def accept(target_logits, draft_probs, draft_tokens, draft_lens=None, *, tempera
         _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if rc != SPEC_OK:
         raise SpecError("spec_accept", rc)
+    return out
+
+
+def accept_sampled_workspace(B: int, K: int, V: int, device) -> torch.Tensor:
+    """A zero-filled workspace for spec_accept_sampled (kept zeroed by the
+    library from call to call)."""
+    n = int(load_library().spec_accept_sampled_workspace_bytes(B, K, V))
+    return torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+
+
+def accept_sampled(target_logits, draft_logits, draft_tokens, draft_lens=None, *,
+                   temperature: float, draft_temperature=None, top_p: float = 1.0,
+                   min_p: float = 0.0, seed: int, offset: int = 0, row_base: int = 0,
+                   workspace=None, out=None, stream=None) -> AcceptResult:
+    """Accept/reject with the draft as logits and the sampler's filters
+    (``spec_accept_sampled``): p' and q' are top-p / min-p filtered tempered
+    softmaxes of target_logits [B, K+1, V] and draft_logits [B, K, V] (same
+    dtype, float32 or bfloat16)."""
+    _check_dev("target_logits", target_logits, ndim=3)
+    if target_logits.dtype == torch.float32:
+        dt = SPEC_F32
+    elif target_logits.dtype == torch.bfloat16:
+        dt = SPEC_BF16
+    else:
+        raise TypeError("target_logits must be float32 or bfloat16")
+    B, K1, V = target_logits.shape
+    K = K1 - 1
+    dev = target_logits.device
+    _check_dev("draft_logits", draft_logits, target_logits.dtype, 3)
+    if tuple(draft_logits.shape) != (B, K, V):
+        raise ValueError("draft_logits must be [B, K, V]")
+    _check_dev("draft_tokens", draft_tokens, torch.int32, 2)
+    if draft_lens is not None:
+        _check_dev("draft_lens", draft_lens, torch.int32, 1)
+    if draft_temperature is None:
+        draft_temperature = temperature
+    if out is None:
+        out = AcceptResult(torch.empty(B, K + 1, dtype=torch.int32, device=dev),
+                           torch.empty(B, dtype=torch.int32, device=dev),
+                           torch.empty(B, K, dtype=torch.float32, device=dev),
+                           torch.empty(B, dtype=torch.int32, device=dev))
+    if workspace is None:
+        workspace = accept_sampled_workspace(B, K, V, dev)
+    rc = load_library().spec_accept_sampled(
+        _ptr(target_logits), _ptr(draft_logits), dt, _ptr(draft_tokens), _ptr(draft_lens), B, K,
+        V, row_base, float(temperature), float(draft_temperature), float(top_p), float(min_p),
+        seed & (2**64 - 1), offset & (2**64 - 1), _ptr(out.tokens), _ptr(out.accepted),
+        _ptr(out.p_draft), _ptr(out.status), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(stream))
+    if rc != SPEC_OK:
+        raise SpecError("spec_accept_sampled", rc)
     return out
 
 

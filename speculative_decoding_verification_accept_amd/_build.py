@@ -28,6 +28,7 @@ COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-I", INCLUDE, "-I", CSRC]
 PER_FILE = {
     "spec_accept.hip": ["-ffp-contract=off"],
+    "spec_accept_sampled.hip": ["-ffp-contract=off"],
     "spec_verify_linear.hip": [],
     "spec_adapt.hip": ["-ffp-contract=off"],
     "spec_plan.cpp": ["-ffp-contract=off"],

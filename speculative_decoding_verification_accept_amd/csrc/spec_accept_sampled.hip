@@ -1,0 +1,712 @@
+// spec_accept_sampled.hip -- accept/reject with the production sampler's
+// filters: the draft arrives as logits, and the target's and the draft's
+// tempered distributions pass through top-p and min-p before the acceptance
+// rule, the residual and the bonus draw.
+//
+// Sources (by page title and section):
+//  * "Decode is memory-bound: ~59 tok/s ceiling on an RTX 4090, and how
+//    speculative decoding beats it" (trefon.com), section "Two things that
+//    follow from the math": the production sampler (temperature 0.6, top-p
+//    0.95, min-p 0.05) and the draft sampler matched to the target's;
+//    section "Speculative decoding": accepting with probability
+//    min(1, p(x)/q(x)) leaves exactly the target distribution.
+//  * "Speculative decoding and early exit ..." (reactapp.top), section
+//    "Speculative decoding: draft first, then verify", listing
+//    speculative_decode: q is the tempered softmax of the draft's logits;
+//    accept/reject, residual resample, bonus token.
+//
+// Filters.  On softmax(z / T): top-p keeps token j iff the mass of the
+// tokens with a strictly larger logit is below top_p; min-p keeps j iff
+// p_j >= min_p max p; kept iff both keep it; the kept mass is renormalised.
+//
+// Two launches, nothing waits:
+//  k_stats   one workgroup per distribution row (target positions 0..L_b,
+//            draft positions 0..L_b-1).  Pass 1: the max m.  Pass 2 (top-p
+//            only): every entry's weight e = 2^(fl(z c - fl(m c))), c =
+//            log2(e)/T, in 2^-32 fixed point (exact, order-free integer
+//            sums) into a histogram of 512 bins of u = m c - z c (1/16 wide;
+//            u >= 32 adds nothing in fixed point), which finds the bin where
+//            the mass from the top first reaches top_p of the total; that
+//            bin's entries are collected in LDS (one LDS atomic per wave),
+//            and a radix select on their order-preserving fp32 keys (4 digits
+//            of 8 bits, fixed-point mass histograms) finds the exact logit
+//            at which the mass reaches top_p: kept iff key(z) >= that key.
+//            Pass 3: the kept mass S' = sum of kept e in fp64, in a fixed
+//            order.  A crossing bin of more than 4096 entries keeps the
+//            whole bin and sets SPEC_ROW_FILTER_COARSE.
+//  k_accept  one workgroup per (row, chunk of 16 KB of logits).  Every
+//            workgroup computes the row's decision itself from the stats and
+//            two gathers per position (p'(x_i), q'(x_i) in fp64, the same
+//            uniforms as spec_accept), then the draw weights of its chunk
+//            at position a_b (residual max(p' - q', 0) after a rejection,
+//            p' for the bonus), publishes per-thread fp64 sums and the chunk
+//            mass, and counts in; the row's last workgroup draws by inverse
+//            CDF in three levels (chunk, thread, entry) and writes the row.
+//            Exchange between workgroups uses agent-scope atomic accesses
+//            (SC1) and a drain of the workgroup's stores before it counts in.
+#include <math.h>
+
+#include "device_common.hpp"
+#include "philox.hpp"
+#include "spec_verify.h"
+
+namespace specv {
+namespace {
+
+typedef uint16_t bf16_t;
+
+constexpr int kT = 256;                     // threads per workgroup
+constexpr int kW = kT / kWave;
+constexpr int kChunkBytes = 16384;
+constexpr int kBins = 512;                  // coarse bins of u, 1/16 wide
+constexpr float kBinScale = 16.f;
+constexpr int kCand = 4096;                 // crossing-bin entries resolved exactly
+constexpr int kMaxChunks = 1024;
+constexpr int kRowStride = 64;              // ints per row record (256 bytes)
+constexpr int kCnt = 0;                     // phase-2 arrivals
+constexpr double kFix = 4294967296.0;       // 2^32
+constexpr int kInvalid = SPEC_ROW_NONFINITE | SPEC_ROW_BAD_TOKEN | SPEC_ROW_BAD_LEN | SPEC_ROW_ZERO_Q;
+
+template <typename T> constexpr int chunk_of() { return kChunkBytes / (int)sizeof(T); }
+template <typename T> constexpr int ept_of() { return chunk_of<T>() / kT; }
+
+__device__ __forceinline__ void co_store(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t co_load(const uint64_t* p) {
+    return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int co_add(int* p, int v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void co_store32(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void drain_vm() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+__device__ __forceinline__ uint64_t dbits(double d) { return (uint64_t)__double_as_longlong(d); }
+__device__ __forceinline__ double bitsd(uint64_t u) { return __longlong_as_double((long long)u); }
+
+template <typename T>
+__device__ __forceinline__ float ld(const T* row, int64_t j) {
+    if constexpr (sizeof(T) == 2) return bf16_to_f32(row[j]);
+    else return row[j];
+}
+
+// order-preserving key of an fp32 value (-0 and +0 share one key)
+__device__ __forceinline__ uint32_t fkey(float z) {
+    const uint32_t u = __float_as_uint(z == 0.f ? 0.f : z);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// weight of logit z relative to the row max: 2^(fl(z c - fl(m c)))
+__device__ __forceinline__ float wexp(float z, float c, float mc) { return hw_exp2(__builtin_fmaf(z, c, -mc)); }
+
+// Stats of one distribution row.
+struct Stat {
+    float m;        // max logit
+    uint32_t tau;   // kept iff fkey(z) >= tau (0: no top-p)
+    double s;       // kept mass sum of e
+    int flag;       // 1: NaN / +Inf / all -Inf
+    int coarse;     // the top-p crossing bin was kept whole
+};
+
+struct Args {
+    const void* z;        // target logits [B, K+1, V]
+    const void* d;        // draft logits [B, K, V]
+    const int32_t* x;     // [B, K]
+    const int32_t* lens;  // [B] or null
+    int64_t B, V, row_base;
+    int K, C;
+    float cp, cq;         // log2(e) / T of the target and of the draft
+    float top_p, min_p;
+    uint64_t seed, offset;
+    int32_t* out_tokens;
+    int32_t* out_accepted;
+    float* out_p_draft;
+    int32_t* out_status;
+    int* rows;            // [B][kRowStride]
+    Stat* stats;          // [B][2K+1]: target 0..K, then draft 0..K-1
+    uint64_t* mass;       // [B][C][2]: draw mass, p' mass (for an empty residual)
+    uint64_t* tsum;       // [B][C][kT]
+};
+
+__device__ __forceinline__ int row_len(const Args& a, int64_t b) { return a.lens ? a.lens[b] : a.K; }
+
+// ---- k_stats ----------------------------------------------------------------------------------
+struct StatShared {
+    unsigned long long hm[kBins];
+    uint32_t hc[kBins];
+    uint32_t ck[kCand];
+    unsigned long long cq[kCand];
+    unsigned long long dig[256];
+    unsigned long long red_u[kW];
+    double red_d[kW];
+    float red_f[kW];
+    int red_i[kW];
+    uint32_t red_k[kW];
+    int ncand, bstar;
+    uint32_t prefix, kmin;
+    double rem;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kT) void k_stats(Args a) {
+    __shared__ StatShared sh;
+    const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
+    const int S2 = 2 * a.K + 1;
+    const int64_t b = blockIdx.x / S2;
+    const int s = (int)(blockIdx.x % S2);
+    const int L = row_len(a, b);
+    if (L < 0 || L > a.K) return;
+    const bool draft = s > a.K;
+    const int pos = draft ? s - a.K - 1 : s;
+    if (draft ? pos >= L : pos > L) return;
+    const int64_t V = a.V;
+    const T* row = draft ? static_cast<const T*>(a.d) + (b * a.K + pos) * V
+                         : static_cast<const T*>(a.z) + (b * (a.K + 1) + pos) * V;
+    const float c = draft ? a.cq : a.cp;
+    Stat st{};
+
+    // pass 1: max, non-finite flag
+    float mx = -INFINITY;
+    int bad = 0;
+    for (int64_t j = t; j < V; j += kT) {
+        const float v = ld(row, j);
+        bad |= (v != v) | (v == INFINITY);
+        mx = fmaxf(mx, v);
+    }
+    mx = wave_max(mx);
+    bad = wave_or(bad);
+    if (lane == 0) {
+        sh.red_f[wv] = mx;
+        sh.red_i[wv] = bad;
+    }
+    __syncthreads();
+    float m = sh.red_f[0];
+    for (int k = 1; k < kW; ++k) {
+        m = fmaxf(m, sh.red_f[k]);
+        bad |= sh.red_i[k];
+    }
+    __syncthreads();
+    st.m = m;
+    if (bad || m == -INFINITY) {
+        if (t == 0) {
+            st.flag = 1;
+            a.stats[b * S2 + s] = st;
+        }
+        return;
+    }
+    const float mc = m * c;
+
+    // pass 2: top-p cut
+    uint32_t tau = 0;
+    if (a.top_p < 1.f) {
+        for (int k = t; k < kBins; k += kT) {
+            sh.hm[k] = 0ull;
+            sh.hc[k] = 0u;
+        }
+        __syncthreads();
+        unsigned long long tot = 0ull;
+        for (int64_t j = t; j < V; j += kT) {
+            const float w = __builtin_fmaf(ld(row, j), c, -mc);   // -u
+            const unsigned long long q = (unsigned long long)(hw_exp2(w) * 4294967296.f);
+            tot += q;
+            const float u = -w;
+            if (u < 32.f && q) {
+                const int bin = (int)(u * kBinScale);
+                atomicAdd(&sh.hm[bin], q);
+                atomicAdd(&sh.hc[bin], 1u);
+            }
+        }
+        // the total over the workgroup (integer: exact in any order)
+        for (int o = kWave / 2; o > 0; o >>= 1) tot += __shfl_xor(tot, o, kWave);
+        if (lane == 0) sh.red_u[wv] = tot;
+        __syncthreads();
+        if (t == 0) {
+            unsigned long long S = 0ull;
+            for (int k = 0; k < kW; ++k) S += sh.red_u[k];
+            const double need = (double)a.top_p * (double)S;
+            unsigned long long acc = 0ull;
+            int bs = kBins - 1;
+            for (int k = 0; k < kBins; ++k) {
+                if ((double)(acc + sh.hm[k]) >= need) {
+                    bs = k;
+                    break;
+                }
+                acc += sh.hm[k];
+            }
+            sh.bstar = bs;
+            sh.rem = need - (double)acc;  // > 0: mass still needed inside the bin
+            sh.ncand = 0;
+            sh.kmin = 0xFFFFFFFFu;
+        }
+        __syncthreads();
+        const int bs = sh.bstar;
+        const bool fits = sh.hc[bs] <= (uint32_t)kCand;
+        // collect the crossing bin's entries (or only their smallest key)
+        for (int64_t j0 = 0; j0 < V; j0 += kT) {
+            const int64_t j = j0 + t;
+            bool in = false;
+            uint32_t key = 0;
+            unsigned long long q = 0;
+            if (j < V) {
+                const float z = ld(row, j);
+                const float w = __builtin_fmaf(z, c, -mc);
+                q = (unsigned long long)(hw_exp2(w) * 4294967296.f);
+                const float u = -w;
+                in = q && u < 32.f && (int)(u * kBinScale) == bs;
+                key = fkey(z);
+            }
+            if (fits) {
+                const uint64_t mask = __ballot(in);
+                if (mask) {
+                    int base = 0;
+                    if (lane == 0) base = atomicAdd(&sh.ncand, __popcll(mask));
+                    base = __shfl(base, 0, kWave);
+                    if (in) {
+                        const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
+                        sh.ck[slot] = key;
+                        sh.cq[slot] = q;
+                    }
+                }
+            } else if (in) {
+                atomicMin(&sh.kmin, key);
+            }
+        }
+        __syncthreads();
+        if (fits) {
+            // radix select, descending: the key at which the mass reaches rem
+            const int n = sh.ncand;
+            uint32_t prefix = 0;
+            double rem = sh.rem;
+            for (int lvl = 0; lvl < 4; ++lvl) {
+                const int shift = 24 - 8 * lvl;
+                sh.dig[t] = 0ull;
+                __syncthreads();
+                for (int k = t; k < n; k += kT) {
+                    const uint32_t key = sh.ck[k];
+                    const bool match = lvl == 0 || (key >> (shift + 8)) == prefix;
+                    if (match) atomicAdd(&sh.dig[(key >> shift) & 255u], sh.cq[k]);
+                }
+                __syncthreads();
+                if (t == 0) {
+                    unsigned long long acc = 0ull;
+                    int dsel = 0;
+                    for (int dd = 255; dd >= 0; --dd) {
+                        if ((double)(acc + sh.dig[dd]) >= rem) {
+                            dsel = dd;
+                            break;
+                        }
+                        acc += sh.dig[dd];
+                    }
+                    sh.prefix = (prefix << 8) | (uint32_t)dsel;
+                    sh.rem = rem - (double)acc;
+                }
+                __syncthreads();
+                prefix = sh.prefix;
+                rem = sh.rem;
+            }
+            tau = prefix;
+        } else {
+            tau = sh.kmin;
+            st.coarse = 1;
+        }
+    }
+
+    // pass 3: kept mass
+    double sum = 0.0;
+    const float minp = a.min_p;
+    for (int64_t j = t; j < V; j += kT) {
+        const float z = ld(row, j);
+        const float e = wexp(z, c, mc);
+        if (fkey(z) >= tau && e >= minp) sum += (double)e;
+    }
+    for (int o = kWave / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+    if (lane == 0) sh.red_d[wv] = sum;
+    __syncthreads();
+    if (t == 0) {
+        double S = 0.0;
+        for (int k = 0; k < kW; ++k) S += sh.red_d[k];
+        st.tau = tau;
+        st.s = S;
+        a.stats[b * S2 + s] = st;
+    }
+}
+
+// ---- k_accept ---------------------------------------------------------------------------------
+struct AccShared {
+    double red_d[kW];
+    int red_x[kW];
+    double w[kMaxChunks];
+    double scan[kT + 1];
+    float px[SPEC_MAX_DRAFT];
+    int status, a, cstar, lastpos;
+    double tp;
+};
+
+// filtered, unnormalised weight of logit z under stats (st, c)
+__device__ __forceinline__ float kept_w(float z, float c, const Stat& st, float minp) {
+    const float e = wexp(z, c, st.m * c);
+    return (fkey(z) >= st.tau && e >= minp) ? e : 0.f;
+}
+
+// draw weight of entry j: the residual after a rejection, p' for the bonus,
+// p' again (pmode 2) when the residual is empty
+template <typename T>
+__device__ __forceinline__ float draw_w(const T* zr, const T* dr, int64_t j, int pmode, const Args& a,
+                                        const Stat& sp, const Stat& sq, float invp, float invq) {
+    const float wp = kept_w(ld(zr, j), a.cp, sp, a.min_p);
+    if (pmode != 0) return wp;
+    const float wq = kept_w(ld(dr, j), a.cq, sq, a.min_p);
+    return fmaxf(wp * invp - wq * invq, 0.f);
+}
+
+__device__ __forceinline__ double block_sum(double v, double* sh) {
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    if ((threadIdx.x & (kWave - 1)) == 0) sh[threadIdx.x / kWave] = v;
+    __syncthreads();
+    double r = 0.0;
+    for (int k = 0; k < kW; ++k) r += sh[k];
+    __syncthreads();
+    return r;
+}
+
+// inclusive scan of one double per thread over the workgroup (fixed order)
+__device__ __forceinline__ double block_scan(double v, double* sh, double* total) {
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    for (int o = 1; o < kWave; o <<= 1) {
+        const double n = __shfl_up(v, o, kWave);
+        if (lane >= o) v += n;
+    }
+    if (lane == kWave - 1) sh[wv] = v;
+    __syncthreads();
+    double base = 0.0, tot = 0.0;
+    for (int k = 0; k < kW; ++k) {
+        if (k < wv) base += sh[k];
+        tot += sh[k];
+    }
+    __syncthreads();
+    *total = tot;
+    return base + v;
+}
+
+// the last index (>= base) whose weight is positive, merged into sh.lastpos
+__device__ __forceinline__ void last_positive(bool pos, int base, AccShared& sh) {
+    const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
+    const uint64_t msk = __ballot(pos);
+    if (lane == 0) sh.red_x[wv] = msk ? wv * kWave + 63 - __clzll((long long)msk) : -1;
+    __syncthreads();
+    if (t == 0) {
+        int l = -1;
+        for (int k = 0; k < kW; ++k) l = max(l, sh.red_x[k]);
+        if (l >= 0) sh.lastpos = max(sh.lastpos, base + l);
+    }
+    __syncthreads();
+}
+
+template <typename T>
+__global__ __launch_bounds__(kT) void k_accept(Args a) {
+    constexpr int CH = chunk_of<T>(), EPT = ept_of<T>();
+    __shared__ AccShared sh;
+    const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
+    const int64_t b = blockIdx.x / a.C;
+    const int ci = (int)(blockIdx.x % a.C);
+    const int K = a.K, S2 = 2 * K + 1;
+    const int64_t V = a.V;
+    const int L = row_len(a, b);
+    const bool writer = ci == 0;
+    if (L < 0 || L > K) {
+        if (writer) {
+            for (int i = t; i <= K; i += kT) a.out_tokens[b * (K + 1) + i] = -1;
+            if (a.out_p_draft)
+                for (int i = t; i < K; i += kT) a.out_p_draft[b * K + i] = -1.f;
+            if (t == 0) {
+                a.out_accepted[b] = -1;
+                if (a.out_status) a.out_status[b] = SPEC_ROW_BAD_LEN;
+            }
+        }
+        return;
+    }
+    const T* zb = static_cast<const T*>(a.z) + b * (K + 1) * V;
+    const T* db = static_cast<const T*>(a.d) + b * K * V;
+    const Stat* stb = a.stats + b * S2;
+    if (t == 0) {
+        sh.status = 0;
+        sh.a = L;
+    }
+    __syncthreads();
+    // the decision, in every workgroup of the row (same inputs, same result)
+    {
+        int st = 0;
+        if (t <= L && stb[t].flag) st |= SPEC_ROW_NONFINITE;
+        if (t < L && stb[K + 1 + t].flag) st |= SPEC_ROW_NONFINITE;
+        if (t < L && !(st & SPEC_ROW_NONFINITE)) {
+            const int x = a.x[b * K + t];
+            float px = -1.f;
+            if (x < 0 || (int64_t)x >= V) {
+                st |= SPEC_ROW_BAD_TOKEN;
+            } else {
+                const Stat sp = stb[t], sq = stb[K + 1 + t];
+                const float zx = ld(zb + (int64_t)t * V, x), dx = ld(db + (int64_t)t * V, x);
+                const bool kp = kept_w(zx, a.cp, sp, a.min_p) > 0.f;
+                const bool kq = kept_w(dx, a.cq, sq, a.min_p) > 0.f;
+                if (!kq) {
+                    st |= SPEC_ROW_ZERO_Q;
+                } else {
+                    const double p = kp ? exp2((double)zx * (double)a.cp - (double)(sp.m * a.cp)) / sp.s : 0.0;
+                    const double q = exp2((double)dx * (double)a.cq - (double)(sq.m * a.cq)) / sq.s;
+                    px = (float)p;
+                    const double acc = fmin(1.0, p / q);
+                    const RowPosUniforms u = row_pos_uniforms(a.seed, a.offset, (uint32_t)(a.row_base + b), (uint32_t)t);
+                    if (!((double)u.acc < acc)) atomicMin(&sh.a, t);
+                }
+            }
+            sh.px[t] = px;
+        }
+        if (st) atomicOr(&sh.status, st);
+    }
+    __syncthreads();
+    int status = sh.status;
+    const int ar = sh.a;
+    const bool invalid = (status & kInvalid) != 0;
+    if (writer && a.out_p_draft)
+        for (int i = t; i < K; i += kT) a.out_p_draft[b * K + i] = (!invalid && i < L) ? sh.px[i] : -1.f;
+    if (invalid) {
+        if (writer) {
+            for (int i = t; i <= K; i += kT) a.out_tokens[b * (K + 1) + i] = -1;
+            if (t == 0) {
+                a.out_accepted[b] = -1;
+                if (a.out_status) a.out_status[b] = status;
+            }
+        }
+        return;
+    }
+    for (int i = 0; i < L + 1; ++i) status |= stb[i].coarse ? SPEC_ROW_FILTER_COARSE : 0;
+    for (int i = 0; i < L; ++i) status |= stb[K + 1 + i].coarse ? SPEC_ROW_FILTER_COARSE : 0;
+
+    // phase 2: this chunk's draw weights at position ar
+    const bool reject = ar < L;
+    const Stat sp = stb[ar];
+    const Stat sq = reject ? stb[K + 1 + ar] : sp;
+    const float invp = (float)(1.0 / sp.s), invq = (float)(1.0 / sq.s);
+    const T* zr = zb + (int64_t)ar * V;
+    const T* dr = db + (int64_t)(reject ? ar : 0) * V;
+    const int64_t chunk0 = (int64_t)ci * CH;
+    const int64_t j0 = chunk0 + (int64_t)t * EPT;
+    double own = 0.0, ownp = 0.0;
+    for (int e = 0; e < EPT; ++e) {
+        const int64_t j = j0 + e;
+        if (j < V) {
+            own += (double)draw_w(zr, dr, j, reject ? 0 : 1, a, sp, sq, invp, invq);
+            if (reject) ownp += (double)kept_w(ld(zr, j), a.cp, sp, a.min_p);
+        }
+    }
+    uint64_t* tsrow = a.tsum + b * a.C * kT;
+    co_store(tsrow + (int64_t)ci * kT + t, dbits(own));
+    const double cm = block_sum(own, sh.red_d);
+    const double cmp = reject ? block_sum(ownp, sh.red_d) : 0.0;
+    if (t == 0) {
+        co_store(a.mass + (b * a.C + ci) * 2, dbits(cm));
+        co_store(a.mass + (b * a.C + ci) * 2 + 1, dbits(cmp));
+    }
+    drain_vm();
+    __syncthreads();
+    int* rowc = a.rows + b * kRowStride;
+    if (t == 0) sh.lastpos = co_add(rowc + kCnt, 1) == a.C - 1;
+    __syncthreads();
+    if (!sh.lastpos) return;
+
+    // the row's last workgroup draws
+    if (t == 0) co_store32(rowc + kCnt, 0);
+    const int C = a.C;
+    int pmode = reject ? 0 : 1;
+    for (int k = t; k < C; k += kT) sh.w[k] = bitsd(co_load(a.mass + (b * C + k) * 2));
+    __syncthreads();
+    double tot;
+    for (;;) {
+        double part = 0.0;
+        for (int k = t; k < C; k += kT) part += sh.w[k];
+        tot = block_sum(part, sh.red_d);
+        if (pmode != 0 || tot > 0.0) break;
+        pmode = 2;  // empty residual: draw from p'
+        status |= SPEC_ROW_RESID_ZERO;
+        for (int k = t; k < C; k += kT) sh.w[k] = bitsd(co_load(a.mass + (b * C + k) * 2 + 1));
+        __syncthreads();
+    }
+    const RowPosUniforms u = row_pos_uniforms(a.seed, a.offset, (uint32_t)(a.row_base + b), (uint32_t)ar);
+    double tp = (double)u.smp * tot;
+    // level 1: the chunk
+    if (t == 0) {
+        sh.cstar = -1;
+        sh.lastpos = -1;
+    }
+    __syncthreads();
+    double carry = 0.0;
+    for (int k0 = 0; k0 < C; k0 += kT) {
+        const int k = k0 + t;
+        const double wk = k < C ? sh.w[k] : 0.0;
+        double btot;
+        const double incl = carry + block_scan(wk, sh.red_d, &btot);
+        sh.scan[t + 1] = incl;
+        if (t == 0) sh.scan[0] = carry;
+        __syncthreads();
+        if (wk > 0.0 && incl > tp && sh.scan[t] <= tp) {
+            sh.cstar = k;
+            sh.tp = tp - sh.scan[t];
+        }
+        last_positive(wk > 0.0, k0, sh);
+        if (sh.cstar >= 0) break;
+        carry += btot;
+    }
+    int cstar = sh.cstar;
+    tp = sh.tp;
+    if (cstar < 0) {
+        cstar = max(sh.lastpos, 0);
+        tp = INFINITY;
+    }
+    __syncthreads();
+    // level 2: the thread of chunk cstar
+    const int64_t cb = (int64_t)cstar * CH;
+    double ts;
+    if (pmode == 2) {
+        ts = 0.0;
+        for (int e = 0; e < EPT; ++e) {
+            const int64_t j = cb + (int64_t)t * EPT + e;
+            if (j < V) ts += (double)draw_w(zr, dr, j, 2, a, sp, sq, invp, invq);
+        }
+    } else {
+        ts = bitsd(co_load(tsrow + (int64_t)cstar * kT + t));
+    }
+    if (t == 0) {
+        sh.cstar = -1;
+        sh.lastpos = -1;
+    }
+    __syncthreads();
+    double ttot;
+    const double incl2 = block_scan(ts, sh.red_d, &ttot);
+    sh.scan[t + 1] = incl2;
+    if (t == 0) sh.scan[0] = 0.0;
+    __syncthreads();
+    if (ts > 0.0 && incl2 > tp && sh.scan[t] <= tp) {
+        sh.cstar = t;
+        sh.tp = tp - sh.scan[t];
+    }
+    last_positive(ts > 0.0, 0, sh);
+    int tstar = sh.cstar;
+    tp = sh.tp;
+    if (tstar < 0) {
+        tstar = max(sh.lastpos, 0);
+        tp = INFINITY;
+    }
+    // level 3: that thread's entries, one per lane of wave 0, in index order
+    if (wv == 0) {
+        const int64_t jb = cb + (int64_t)tstar * EPT;
+        const int64_t j = jb + lane;
+        const float wl = (lane < EPT && j < V) ? draw_w(zr, dr, j, pmode, a, sp, sq, invp, invq) : 0.f;
+        double incl3 = (double)wl;
+        for (int o = 1; o < kWave; o <<= 1) {
+            const double n = __shfl_up(incl3, o, kWave);
+            if (lane >= o) incl3 += n;
+        }
+        const uint64_t hit = __ballot(wl > 0.f && incl3 > tp);
+        const uint64_t pos = __ballot(wl > 0.f);
+        const int sel = hit ? __ffsll((long long)hit) - 1 : (pos ? 63 - __clzll((long long)pos) : 0);
+        if (lane == 0) {
+            a.out_tokens[b * (K + 1) + ar] = (int32_t)(jb + sel);
+            a.out_accepted[b] = ar;
+            if (a.out_status) a.out_status[b] = status;
+        }
+    }
+    for (int i = t; i <= K; i += kT)
+        if (i != ar) a.out_tokens[b * (K + 1) + i] = (i < ar) ? a.x[b * K + i] : -1;
+}
+
+struct Ws {
+    size_t rows_off, stats_off, mass_off, tsum_off, total;
+};
+
+Ws ws_layout(int64_t B, int K, int64_t V) {
+    const int64_t C = (V + kChunkBytes / 4 - 1) / (kChunkBytes / 4);  // the most chunks of either dtype
+    Ws w;
+    w.rows_off = 0;
+    w.stats_off = align_up((size_t)B * kRowStride * sizeof(int), 256);
+    w.mass_off = w.stats_off + align_up((size_t)B * (2 * K + 1) * sizeof(Stat), 256);
+    w.tsum_off = w.mass_off + align_up((size_t)B * C * 2 * 8, 256);
+    w.total = w.tsum_off + align_up((size_t)B * C * kT * 8, 256);
+    return w;
+}
+
+}  // namespace
+}  // namespace specv
+
+using namespace specv;
+
+extern "C" size_t spec_accept_sampled_workspace_bytes(int64_t B, int K, int64_t V) {
+    if (B < 0 || K < 0 || K > SPEC_MAX_DRAFT || V < 1) return 0;
+    return ws_layout(B, K, V).total;
+}
+
+extern "C" int spec_accept_sampled(const void* target_logits, const void* draft_logits,
+                                   int logits_dtype, const int32_t* draft_tokens,
+                                   const int32_t* draft_lens, int64_t B, int K, int64_t V,
+                                   int64_t row_base, float temperature, float draft_temperature,
+                                   float top_p, float min_p, uint64_t philox_seed,
+                                   uint64_t philox_offset, int32_t* out_tokens,
+                                   int32_t* out_accepted, float* out_p_draft, int32_t* out_status,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+    if (B < 0 || K < 0 || K > SPEC_MAX_DRAFT || V < 1 || V > 0x7FFFFFFF || row_base < 0)
+        return SPEC_ERR_INVALID_ARG;
+    if (row_base + B > ((int64_t)1 << 32)) return SPEC_ERR_INVALID_ARG;
+    if (logits_dtype != SPEC_F32 && logits_dtype != SPEC_BF16) return SPEC_ERR_INVALID_ARG;
+    auto finite_pos = [](float v) { return v > 0.f && v < INFINITY; };
+    if (!finite_pos(temperature) || !finite_pos(draft_temperature)) return SPEC_ERR_INVALID_ARG;
+    if (!(top_p > 0.f && top_p <= 1.f) || !(min_p >= 0.f && min_p < 1.f)) return SPEC_ERR_INVALID_ARG;
+    if (B == 0) return SPEC_OK;
+    if (!target_logits || !out_tokens || !out_accepted) return SPEC_ERR_INVALID_ARG;
+    if (K > 0 && (!draft_logits || !draft_tokens)) return SPEC_ERR_INVALID_ARG;
+    const int64_t CH = logits_dtype == SPEC_BF16 ? chunk_of<bf16_t>() : chunk_of<float>();
+    const int64_t C = (V + CH - 1) / CH;
+    if (C > kMaxChunks || B * C > ((int64_t)1 << 26) || B * (2 * K + 1) > ((int64_t)1 << 31) - 1)
+        return SPEC_ERR_INVALID_ARG;
+    const Ws lay = ws_layout(B, K, V);
+    if (!workspace || workspace_bytes < lay.total || ((uintptr_t)workspace & 15)) return SPEC_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    Args a{};
+    a.z = target_logits;
+    a.d = draft_logits;
+    a.x = draft_tokens;
+    a.lens = draft_lens;
+    a.B = B;
+    a.V = V;
+    a.row_base = row_base;
+    a.K = K;
+    a.C = (int)C;
+    a.cp = (float)(1.4426950408889634074 / (double)temperature);
+    a.cq = (float)(1.4426950408889634074 / (double)draft_temperature);
+    a.top_p = top_p;
+    a.min_p = min_p;
+    a.seed = philox_seed;
+    a.offset = philox_offset;
+    a.out_tokens = out_tokens;
+    a.out_accepted = out_accepted;
+    a.out_p_draft = out_p_draft;
+    a.out_status = out_status;
+    a.rows = reinterpret_cast<int*>(ws + lay.rows_off);
+    a.stats = reinterpret_cast<Stat*>(ws + lay.stats_off);
+    a.mass = reinterpret_cast<uint64_t*>(ws + lay.mass_off);
+    a.tsum = reinterpret_cast<uint64_t*>(ws + lay.tsum_off);
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const dim3 gs((unsigned)(B * (2 * K + 1))), ga((unsigned)(B * C));
+    if (logits_dtype == SPEC_BF16) {
+        hipLaunchKernelGGL(k_stats<bf16_t>, gs, dim3(kT), 0, s, a);
+        hipLaunchKernelGGL(k_accept<bf16_t>, ga, dim3(kT), 0, s, a);
+    } else {
+        hipLaunchKernelGGL(k_stats<float>, gs, dim3(kT), 0, s, a);
+        hipLaunchKernelGGL(k_accept<float>, ga, dim3(kT), 0, s, a);
+    }
+    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
+}

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
                           "spec_verify_linear_workspace_bytes", "spec_status_string",
                           "spec_abi_version", "spec_adapt", "spec_adapt_state_bytes",
                           "spec_adapt_telemetry_bytes", "spec_plan_depth",
-                          "spec_verify_attention", "spec_verify_attention_workspace_bytes"]), fns
+                          "spec_verify_attention", "spec_verify_attention_workspace_bytes",
+                          "spec_accept_sampled", "spec_accept_sampled_workspace_bytes"]), fns
     assert sorted(n for n, _, _ in sv.ABI) == fns
 
 
@@ -203,3 +204,34 @@ def test_attention_argument_validation(lib):
     n = lib.spec_verify_attention_workspace_bytes(1, 7, 32, 8, 32768)
     assert n >= 8 * 2 * 32 * 128 * 4
     assert lib.spec_verify_attention_workspace_bytes(1, 8, 8, 2, 64) == 0   # invalid shape
+
+
+def _sampled(lib, **kw):
+    a = dict(z=FAKE, d=FAKE, dt=1, x=FAKE, L=None, B=2, K=3, V=1000, rb=0, T=0.6, Td=0.6, tp=0.95,
+             mp=0.05, seed=1, off=0, ot=FAKE, oa=FAKE, op=None, os=None, ws=FAKE, wsb=1 << 30, st=None)
+    a.update(kw)
+    return lib.spec_accept_sampled(a["z"], a["d"], a["dt"], a["x"], a["L"], a["B"], a["K"], a["V"],
+                                   a["rb"], a["T"], a["Td"], a["tp"], a["mp"], a["seed"], a["off"],
+                                   a["ot"], a["oa"], a["op"], a["os"], a["ws"], a["wsb"], a["st"])
+
+
+def test_accept_sampled_argument_validation(lib):
+    E = sv.SPEC_ERR_INVALID_ARG
+    assert _sampled(lib, T=0.0) == E            # no greedy mode here
+    assert _sampled(lib, Td=-1.0) == E
+    assert _sampled(lib, T=float("inf")) == E
+    assert _sampled(lib, tp=0.0) == E
+    assert _sampled(lib, tp=1.5) == E
+    assert _sampled(lib, mp=1.0) == E
+    assert _sampled(lib, mp=-0.1) == E
+    assert _sampled(lib, tp=float("nan")) == E
+    assert _sampled(lib, dt=5) == E
+    assert _sampled(lib, K=256) == E
+    assert _sampled(lib, d=None) == E
+    assert _sampled(lib, x=None) == E
+    assert _sampled(lib, z=None) == E
+    assert _sampled(lib, ws=None) == sv.SPEC_ERR_WORKSPACE
+    assert _sampled(lib, wsb=8) == sv.SPEC_ERR_WORKSPACE
+    assert _sampled(lib, B=0) == sv.SPEC_OK
+    n = lib.spec_accept_sampled_workspace_bytes(64, 7, 128256)
+    assert n >= 64 * 256 + 64 * 15 * 32

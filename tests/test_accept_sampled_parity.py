@@ -1,0 +1,210 @@
+"""spec_accept_sampled on the GPU against the filtered oracle
+(oracle/sampled.py): decisions, emitted tokens and status bits match exactly
+on every row whose decisions (filter cut, acceptance test, draw) lie clear of
+their thresholds by 1e-6; p'(x) within 1e-5 relative.
+
+Definition: page "Decode is memory-bound ..." (trefon.com), section "Two
+things that follow from the math" (production sampler: temperature 0.6,
+top-p 0.95, min-p 0.05) and section "Speculative decoding" (acceptance rule);
+page "Speculative decoding and early exit ..." (reactapp.top), listing
+speculative_decode (draft distribution from the draft's logits).
+"""
+import numpy as np
+import pytest
+import scipy.stats
+import torch
+
+import oracle
+import speculative_decoding_verification_accept_amd as sv
+from oracle import sampled as S
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    oracle.build()
+    oracle.set_mutation(0)
+    sv.load_library()
+
+
+def make_inputs(B, K, V, *, std, noise, T, top_p, min_p, seed, bf16=False, ragged=False):
+    """Target logits ~ N(0, std^2), draft logits = target + N(0, noise^2)
+    (rounded to the dtype), draft tokens drawn from the oracle's filtered
+    draft distribution q' (the drafter's own sampling)."""
+    rng = np.random.default_rng(seed)
+    z = rng.normal(0, std, (B, K + 1, V)).astype(np.float32)
+    d = (z[:, :K] + rng.normal(0, noise, (B, K, V))).astype(np.float32)
+    if bf16:
+        z = torch.from_numpy(z).to(torch.bfloat16).float().numpy()
+        d = torch.from_numpy(d).to(torch.bfloat16).float().numpy()
+    x = np.zeros((B, K), np.int32)
+    for b in range(B):
+        for i in range(K):
+            q = S.filtered(d[b, i], T, float(np.float32(top_p)), float(np.float32(min_p)))[0]
+            x[b, i] = rng.choice(V, p=q / q.sum())
+    L = rng.integers(0, K + 1, B).astype(np.int32) if ragged else np.full(B, K, np.int32)
+    return z, d, x, L
+
+
+def run(z, d, x, L, *, T, Td=None, top_p, min_p, seed, offset, bf16=False, row_base=0, label=""):
+    Td = T if Td is None else Td
+    dt = torch.bfloat16 if bf16 else torch.float32
+    dev = torch.device("cuda:0")
+    B, K1, V = z.shape
+    print(f"[spec_accept_sampled] {label} B={B} K={K1 - 1} V={V} {dt} T={T} top_p={top_p} min_p={min_p}",
+          flush=True)
+    zt = torch.from_numpy(np.ascontiguousarray(z)).to(dt).to(dev)
+    dtt = torch.from_numpy(np.ascontiguousarray(d)).to(dt).to(dev)
+    res = sv.accept_sampled(zt, dtt, torch.from_numpy(x).to(dev),
+                            None if L is None else torch.from_numpy(L).to(dev), temperature=T,
+                            draft_temperature=Td, top_p=top_p, min_p=min_p, seed=seed,
+                            offset=offset, row_base=row_base)
+    torch.cuda.synchronize()
+    g = {k: getattr(res, k).cpu().numpy() for k in ("tokens", "accepted", "p_draft", "status")}
+    o = S.spec_accept_sampled(z, d, x, L, T, Td, top_p, min_p, seed, offset, row_base=row_base)
+    return g, o
+
+
+def compare(g, o, label, max_near=0.05):
+    near = o["near"]
+    ok = ~near
+    assert near.mean() <= max_near, (label, near.mean())
+    st_g = g["status"] & ~sv.ROW_FILTER_COARSE
+    assert np.array_equal(st_g[ok], o["status"][ok]), (label, np.nonzero(st_g[ok] != o["status"][ok]))
+    assert np.array_equal(g["accepted"][ok], o["accepted"][ok]), label
+    assert np.array_equal(g["tokens"][ok], o["tokens"][ok]), label
+    m = ok[:, None] & (o["p_draft"] >= 0)
+    pg, po = g["p_draft"][m].astype(np.float64), o["p_draft"][m]
+    assert np.all(np.abs(pg - po) <= 1e-5 * np.maximum(po, 1e-30) + 1e-12), label
+    assert np.all(g["p_draft"][~(o["p_draft"] >= 0) & ok[:, None]] == -1.0)
+    return dict(rows=len(ok), near=int(near.sum()), accepted_mean=float(o["accepted"][ok].mean()))
+
+
+@pytest.mark.parametrize("top_p,min_p", [(0.95, 0.05), (1.0, 0.0), (0.9, 0.0), (1.0, 0.1), (0.5, 0.02)])
+def test_mid_fp32(top_p, min_p):
+    z, d, x, L = make_inputs(8, 4, 32000, std=3.0, noise=1.0, T=0.6, top_p=top_p, min_p=min_p, seed=2)
+    g, o = run(z, d, x, L, T=0.6, top_p=top_p, min_p=min_p, seed=7, offset=1, label="mid")
+    print(compare(g, o, ("mid", top_p, min_p)))
+
+
+def test_many_rows_bf16_ragged():
+    z, d, x, L = make_inputs(48, 5, 20000, std=2.0, noise=1.0, T=0.8, top_p=0.95, min_p=0.05,
+                             seed=3, bf16=True, ragged=True)
+    g, o = run(z, d, x, L, T=0.8, top_p=0.95, min_p=0.05, seed=11, offset=4, bf16=True, label="ragged")
+    st = compare(g, o, "ragged")
+    print(st)
+    assert np.any(o["accepted"] < L) and np.any(o["accepted"] == L)
+
+
+def test_at_scale_vocab_bf16():
+    # the at-scale vocabulary (V = 128256, bf16), a batch the oracle finishes quickly
+    z, d, x, L = make_inputs(6, 7, 128256, std=3.0, noise=1.5, T=0.8, top_p=0.95, min_p=0.05,
+                             seed=4, bf16=True, ragged=True)
+    g, o = run(z, d, x, L, T=0.8, top_p=0.95, min_p=0.05, seed=5, offset=9, bf16=True, label="scale")
+    print(compare(g, o, "scale"))
+
+
+def test_flat_distribution_deep_top_p_cut():
+    # small logit spread: the top-p cut falls deep in the vocabulary, in a
+    # crossing bin with many entries.  Distinct logits then sit ~3e-5 of mass
+    # apart, so a cut within the 1e-6 window of top_p is not rare (~7% per
+    # distribution): more rows, a looser budget for near-threshold rows.
+    z, d, x, L = make_inputs(16, 3, 30000, std=0.3, noise=0.1, T=1.0, top_p=0.9, min_p=0.0, seed=6)
+    g, o = run(z, d, x, L, T=1.0, top_p=0.9, min_p=0.0, seed=3, offset=0, label="flat")
+    st = compare(g, o, "flat", max_near=0.6)
+    print(st)
+    assert st["rows"] - st["near"] >= 6
+
+
+def test_different_draft_temperature_and_edges():
+    for (B, K, V, bf16) in [(5, 3, 7, False), (4, 0, 500, False), (3, 2, 1, False), (6, 3, 8195, True),
+                            (4, 2, 16384 + 5, False)]:
+        z, d, x, L = make_inputs(B, K, V, std=2.0, noise=0.5, T=0.7, top_p=0.9, min_p=0.05,
+                                 seed=100 + V % 13, bf16=bf16)
+        # the drafter samples at its own temperature
+        rng = np.random.default_rng(V)
+        for b in range(B):
+            for i in range(K):
+                q = S.filtered(d[b, i], 1.3, 0.9, float(np.float32(0.05)))[0]
+                x[b, i] = rng.choice(V, p=q / q.sum())
+        g, o = run(z, d, x, L, T=0.7, Td=1.3, top_p=0.9, min_p=0.05, seed=2, offset=5, bf16=bf16,
+                   label=f"edge {B},{K},{V}")
+        compare(g, o, ("edge", B, K, V), max_near=0.5)
+
+
+def test_status_bits():
+    z, d, x, L = make_inputs(8, 3, 9000, std=2.0, noise=1.0, T=1.0, top_p=0.95, min_p=0.05, seed=8)
+    z[0, 1, 17] = np.nan
+    d[1, 2, 40] = np.inf
+    x[2, 0] = 9000                        # out of range
+    L[3] = 4                              # > K
+    q = S.filtered(d[4, 1], 1.0, 0.95, float(np.float32(0.05)))[1]
+    x[4, 1] = int(np.nonzero(~q)[0][0])   # outside the draft's kept set
+    z[5, 3, 100] = np.nan                 # past L below: not read
+    L[5] = 2
+    g, o = run(z, d, x, L, T=1.0, top_p=0.95, min_p=0.05, seed=1, offset=0, label="status")
+    assert list(o["status"][:6]) == [1, 1, 2, 4, 8, 0]
+    assert list(g["status"][:6] & ~sv.ROW_FILTER_COARSE) == [1, 1, 2, 4, 8, 0]
+    assert np.all(g["accepted"][:5] == -1) and np.all(g["tokens"][:5] == -1)
+    # at T = 1 a top-p cut within 1e-6 of 0.95 is a few-percent event per
+    # distribution, and a row has seven: a looser budget for near rows
+    compare(g, o, "status", max_near=0.5)
+
+
+def test_tiny_vocab_distribution_and_parity():
+    # V = 8, 2*10^5 rounds as rows: GPU decisions match the oracle's and every
+    # emitted position follows the filtered target distribution
+    rounds, K, V, T, tp, mp = 200_000, 3, 8, 0.9, 0.95, 0.05
+    rng = np.random.default_rng(12)
+    z1 = rng.normal(0, 1.5, (K + 1, V)).astype(np.float32)
+    d1 = (z1[:K] + rng.normal(0, 1.0, (K, V))).astype(np.float32)
+    qf = [S.filtered(d1[i], T, tp, float(np.float32(mp)))[0] for i in range(K)]
+    x = np.stack([rng.choice(V, size=rounds, p=qf[i] / qf[i].sum()) for i in range(K)], 1).astype(np.int32)
+    z = np.ascontiguousarray(np.broadcast_to(z1, (rounds, K + 1, V)))
+    d = np.ascontiguousarray(np.broadcast_to(d1, (rounds, K, V)))
+    dev = torch.device("cuda:0")
+    res = sv.accept_sampled(torch.from_numpy(z).to(dev), torch.from_numpy(d).to(dev),
+                            torch.from_numpy(x).to(dev), temperature=T, top_p=tp, min_p=mp,
+                            seed=21, offset=0)
+    torch.cuda.synchronize()
+    tok, acc = res.tokens.cpu().numpy(), res.accepted.cpu().numpy()
+    pv = []
+    for j in range(K + 1):
+        pj = S.filtered(z1[j], T, tp, float(np.float32(mp)))[0]
+        t = tok[acc >= j, j]
+        cnt = np.bincount(t, minlength=V)
+        sup = pj > 0
+        assert cnt[~sup].sum() == 0
+        if sup.sum() > 1:
+            pv.append(scipy.stats.chisquare(cnt[sup], pj[sup] * cnt.sum()).pvalue)
+    assert min(pv) > 1e-4 / len(pv), pv
+    # parity on the first 3000 rounds
+    o = S.spec_accept_sampled(z[:3000], d[:3000], x[:3000], None, T, T, tp, mp, 21, 0)
+    g = {"tokens": tok[:3000], "accepted": acc[:3000], "p_draft": res.p_draft[:3000].cpu().numpy(),
+         "status": res.status[:3000].cpu().numpy()}
+    compare(g, o, "tiny")
+
+
+def test_deterministic_and_row_shard_invariant():
+    z, d, x, L = make_inputs(12, 4, 12000, std=3.0, noise=1.0, T=0.6, top_p=0.95, min_p=0.05,
+                             seed=15, bf16=True, ragged=True)
+    dev = torch.device("cuda:0")
+    zt = torch.from_numpy(z).to(torch.bfloat16).to(dev)
+    dtt = torch.from_numpy(d).to(torch.bfloat16).to(dev)
+    xt, Lt = torch.from_numpy(x).to(dev), torch.from_numpy(L).to(dev)
+    kw = dict(temperature=0.6, top_p=0.95, min_p=0.05, seed=3, offset=2)
+    a1 = sv.accept_sampled(zt, dtt, xt, Lt, **kw)
+    a2 = sv.accept_sampled(zt, dtt, xt, Lt, **kw)
+    h = 5
+    lo = sv.accept_sampled(zt[:h].contiguous(), dtt[:h].contiguous(), xt[:h].contiguous(),
+                           Lt[:h].contiguous(), row_base=0, **kw)
+    hi = sv.accept_sampled(zt[h:].contiguous(), dtt[h:].contiguous(), xt[h:].contiguous(),
+                           Lt[h:].contiguous(), row_base=h, **kw)
+    torch.cuda.synchronize()
+    for f in ("tokens", "accepted", "p_draft", "status"):
+        u, v = getattr(a1, f), getattr(a2, f)
+        assert torch.equal(u, v), f
+        assert torch.equal(u, torch.cat([getattr(lo, f), getattr(hi, f)])), f
