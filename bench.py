@@ -50,7 +50,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-breakdown", action="store_true", help="time the step only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "accept", "gemm", "adapt", "attn"], default=None,
+    ap.add_argument("--only", choices=["step", "accept", "gemm", "adapt", "attn", "sampled"], default=None,
                     help="run one part only (for profiling)")
     return ap.parse_args()
 
@@ -153,6 +153,47 @@ def bench_accept_large(torch, sv, workloads, reps=60, nsets=5):
                 us_per_call=us, positions_per_call=pos, positions_per_s=pos / us * 1e6,
                 algorithmic_bytes=b, achieved_GBs=b / us * 1e-3,
                 frac_hbm=b / us * 1e-3 / HBM_PEAK_GBS)
+
+
+def bench_accept_sampled(torch, sv, workloads, reps=30, nsets=4):
+    """Accept/reject with the draft as logits and the production sampler's
+    filters (temperature 0.8 here as in the at-scale workload, top-p 0.95,
+    min-p 0.05) at B=64, K=7, V=128256 bf16, ragged draft lengths."""
+    dev = torch.device("cuda:0")
+    B, K, V = 64, 7, 128256
+    sets = [workloads.sampled_accept_device(4000 + s, dev) for s in range(nsets)]
+    ws = sv.accept_sampled_workspace(B, K, V, dev)
+    out = sv.AcceptResult(torch.empty(B, K + 1, dtype=torch.int32, device=dev),
+                          torch.empty(B, dtype=torch.int32, device=dev),
+                          torch.empty(B, K, dtype=torch.float32, device=dev),
+                          torch.empty(B, dtype=torch.int32, device=dev))
+    kw = dict(temperature=0.8, top_p=0.95, min_p=0.05, seed=77, workspace=ws, out=out)
+    rows = []
+    for s, (z, d, x, L) in enumerate(sets):
+        sv.accept_sampled(z, d, x, L, offset=s, **kw)
+        torch.cuda.synchronize()
+        Lh = L.cpu().long()
+        rows.append(int((Lh + 1).sum()) + int(Lh.sum()))
+    t0, t1 = _events(torch, 2)
+    t0.record()
+    for r in range(reps):
+        z, d, x, L = sets[r % nsets]
+        sv.accept_sampled(z, d, x, L, offset=r, **kw)
+    t1.record()
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / reps
+    nrows = sum(rows) / nsets
+    # every target row 0..L_b and draft row 0..L_b-1 read once, plus the
+    # token gathers and outputs
+    byts = nrows * V * 2 + B * (K + 2) * 4
+    gbs = byts / us * 1e-3
+    return dict(workload="spec_accept_sampled B=64 K=7 V=128256 bf16 target and draft logits, "
+                         "T=0.8, top-p 0.95, min-p 0.05, ragged L~U{1..7}, draft = its top logit, "
+                         f"{nsets} rotating sets",
+                us_per_call=round(us, 2), distributions_per_call=nrows,
+                positions_per_s=round((nrows + B) / 2 / us * 1e6, 1),
+                algorithmic_bytes=byts, achieved_GBs=round(gbs, 1),
+                frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
 
 
 def bench_gemm_sweep(torch, sv, workloads, reps=40, ncopies=5):
@@ -361,6 +402,9 @@ def main():
     if args.only == "gemm":
         print(json.dumps(bench_gemm_sweep(torch, sv, workloads)))
         return
+    if args.only == "sampled":
+        print(json.dumps(bench_accept_sampled(torch, sv, workloads)))
+        return
     if args.only == "attn":
         print(json.dumps(bench_attention(torch, sv, workloads)))
         return
@@ -406,7 +450,9 @@ def main():
         acc = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in acc.items()}
         acc["traffic_bytes"] = counted["accept_bytes"] if counted else None
         sweep = bench_gemm_sweep(torch, sv, workloads)
-        line["breakdown"] = {"accept_at_scale": acc, "gemm_sweep": sweep,
+        line["breakdown"] = {"accept_at_scale": acc,
+                             "accept_sampled_at_scale": bench_accept_sampled(torch, sv, workloads),
+                             "gemm_sweep": sweep,
                              "verify_attention": bench_attention(torch, sv, workloads),
                              "control": bench_control(torch, sv, sweep["sweep"])}
     if not args.no_cpu_baseline:

@@ -23,9 +23,9 @@
 //  k_stats   one workgroup per distribution row (target positions 0..L_b,
 //            draft positions 0..L_b-1).  Pass 1: the max m.  Pass 2 (top-p
 //            only): every entry's weight e = 2^(fl(z c - fl(m c))), c =
-//            log2(e)/T, in 2^-32 fixed point (exact, order-free integer
+//            log2(e)/T, in 2^-40 fixed point (exact, order-free integer
 //            sums) into a histogram of 512 bins of u = m c - z c (1/16 wide;
-//            u >= 32 adds nothing in fixed point), which finds the bin where
+//            entries past u = 32 count in the total only), which finds the bin where
 //            the mass from the top first reaches top_p of the total; that
 //            bin's entries are collected in LDS (one LDS atomic per wave),
 //            and a radix select on their order-preserving fp32 keys (4 digits
@@ -34,6 +34,11 @@
 //            Pass 3: the kept mass S' = sum of kept e in fp64, in a fixed
 //            order.  A crossing bin of more than 4096 entries keeps the
 //            whole bin and sets SPEC_ROW_FILTER_COARSE.
+//            With min-p on, pass 2 instead collects the entries that pass
+//            min-p (every larger logit passes too), with the row's total
+//            mass; top-p is resolved among them by the same radix select and
+//            S' is their integer kept sum: two passes, unless more than 4096
+//            entries pass min-p (then the general passes run).
 //  k_accept  one workgroup per (row, chunk of 16 KB of logits).  Every
 //            workgroup computes the row's decision itself from the stats and
 //            two gathers per position (p'(x_i), q'(x_i) in fp64, the same
@@ -64,7 +69,6 @@ constexpr int kCand = 4096;                 // crossing-bin entries resolved exa
 constexpr int kMaxChunks = 1024;
 constexpr int kRowStride = 64;              // ints per row record (256 bytes)
 constexpr int kCnt = 0;                     // phase-2 arrivals
-constexpr double kFix = 4294967296.0;       // 2^32
 constexpr int kInvalid = SPEC_ROW_NONFINITE | SPEC_ROW_BAD_TOKEN | SPEC_ROW_BAD_LEN | SPEC_ROW_ZERO_Q;
 
 template <typename T> constexpr int chunk_of() { return kChunkBytes / (int)sizeof(T); }
@@ -137,24 +141,123 @@ struct Args {
 __device__ __forceinline__ int row_len(const Args& a, int64_t b) { return a.lens ? a.lens[b] : a.K; }
 
 // ---- k_stats ----------------------------------------------------------------------------------
+constexpr int kTS = 512;                    // threads of a statistics workgroup
+constexpr int kWS = kTS / kWave;
+constexpr int kU = 4;                       // 16-byte loads per thread in flight per round
+constexpr float kFix40 = 1099511627776.f;   // 2^40: fixed-point unit of the mass histograms
+
 struct StatShared {
     unsigned long long hm[kBins];
     uint32_t hc[kBins];
     uint32_t ck[kCand];
     unsigned long long cq[kCand];
     unsigned long long dig[256];
-    unsigned long long red_u[kW];
-    double red_d[kW];
-    float red_f[kW];
-    int red_i[kW];
-    uint32_t red_k[kW];
+    unsigned long long red_u[kWS];
+    double red_d[kWS];
+    float red_f[kWS];
+    int red_i[kWS];
     int ncand, bstar;
     uint32_t prefix, kmin;
     double rem;
 };
 
-template <typename T>
-__global__ __launch_bounds__(kT) void k_stats(Args a) {
+__device__ __forceinline__ void unpack_vec(const uint4& r, float* z, bf16_t) {
+    z[0] = bf16_lo(r.x); z[1] = bf16_hi(r.x); z[2] = bf16_lo(r.y); z[3] = bf16_hi(r.y);
+    z[4] = bf16_lo(r.z); z[5] = bf16_hi(r.z); z[6] = bf16_lo(r.w); z[7] = bf16_hi(r.w);
+}
+__device__ __forceinline__ void unpack_vec(const uint4& r, float* z, float) {
+    z[0] = __uint_as_float(r.x); z[1] = __uint_as_float(r.y);
+    z[2] = __uint_as_float(r.z); z[3] = __uint_as_float(r.w);
+}
+
+// Calls f(z, j, valid) for every entry j of a row, in rounds of kU loads per
+// thread issued before use.  Every thread runs the same rounds and the same
+// calls (valid is false past the row): f may use wave-wide operations.
+// Loads past the end re-read the last in-range vector instead of branching.
+template <typename T, bool VEC, typename F>
+__device__ __forceinline__ void row_pass(const T* row, int64_t V, F&& f) {
+    const int t = threadIdx.x;
+    if constexpr (VEC) {
+        constexpr int W = 16 / (int)sizeof(T);
+        const int64_t nv = V / W;
+        const uint4* p = reinterpret_cast<const uint4*>(row);
+        for (int64_t v0 = 0; v0 < nv; v0 += (int64_t)kTS * kU) {
+            uint4 r[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) r[u] = p[min(v0 + (int64_t)u * kTS + t, nv - 1)];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t v = v0 + (int64_t)u * kTS + t;
+                float z[W];
+                unpack_vec(r[u], z, T{});
+#pragma unroll
+                for (int k = 0; k < W; ++k) f(z[k], v * W + k, v < nv);
+            }
+        }
+    } else {
+        for (int64_t j0 = 0; j0 < V; j0 += (int64_t)kTS * kU) {
+            float z[kU];
+#pragma unroll
+            for (int u = 0; u < kU; ++u) z[u] = ld(row, min(j0 + (int64_t)u * kTS + t, V - 1));
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                const int64_t j = j0 + (int64_t)u * kTS + t;
+                f(z[u], j, j < V);
+            }
+        }
+    }
+}
+
+// Radix select, descending, over the n collected entries (keys sh.ck, masses
+// sh.cq): the key at which the mass, counted from the largest key down and
+// taking equal keys together, first reaches rem.  Four 8-bit digits.
+__device__ __forceinline__ uint32_t radix_cut(StatShared& sh, int n, double rem) {
+    const int t = threadIdx.x;
+    uint32_t prefix = 0;
+    for (int lvl = 0; lvl < 4; ++lvl) {
+        const int shift = 24 - 8 * lvl;
+        if (t < 256) sh.dig[t] = 0ull;
+        __syncthreads();
+        for (int k = t; k < n; k += kTS) {
+            const uint32_t key = sh.ck[k];
+            if (lvl == 0 || (key >> (shift + 8)) == prefix) atomicAdd(&sh.dig[(key >> shift) & 255u], sh.cq[k]);
+        }
+        __syncthreads();
+        if (t == 0) {
+            unsigned long long acc = 0ull;
+            int dsel = 0;
+            for (int dd = 255; dd >= 0; --dd) {
+                if ((double)(acc + sh.dig[dd]) >= rem) {
+                    dsel = dd;
+                    break;
+                }
+                acc += sh.dig[dd];
+            }
+            sh.prefix = (prefix << 8) | (uint32_t)dsel;
+            sh.rem = rem - (double)acc;
+        }
+        __syncthreads();
+        prefix = sh.prefix;
+        rem = sh.rem;
+    }
+    return prefix;
+}
+
+// Sum over the workgroup of one uint64 per thread (exact, any order).
+__device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v, StatShared& sh) {
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    __syncthreads();
+    if (lane == 0) sh.red_u[wv] = v;
+    __syncthreads();
+    unsigned long long r = 0ull;
+    for (int k = 0; k < kWS; ++k) r += sh.red_u[k];
+    __syncthreads();
+    return r;
+}
+
+template <typename T, bool VEC>
+__global__ __launch_bounds__(kTS) void k_stats(Args a) {
     __shared__ StatShared sh;
     const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
     const int S2 = 2 * a.K + 1;
@@ -174,11 +277,12 @@ __global__ __launch_bounds__(kT) void k_stats(Args a) {
     // pass 1: max, non-finite flag
     float mx = -INFINITY;
     int bad = 0;
-    for (int64_t j = t; j < V; j += kT) {
-        const float v = ld(row, j);
-        bad |= (v != v) | (v == INFINITY);
-        mx = fmaxf(mx, v);
-    }
+    row_pass<T, VEC>(row, V, [&](float z, int64_t, bool ok) {
+        if (ok) {
+            bad |= (z != z) | (z == INFINITY);
+            mx = fmaxf(mx, z);
+        }
+    });
     mx = wave_max(mx);
     bad = wave_or(bad);
     if (lane == 0) {
@@ -187,7 +291,7 @@ __global__ __launch_bounds__(kT) void k_stats(Args a) {
     }
     __syncthreads();
     float m = sh.red_f[0];
-    for (int k = 1; k < kW; ++k) {
+    for (int k = 1; k < kWS; ++k) {
         m = fmaxf(m, sh.red_f[k]);
         bad |= sh.red_i[k];
     }
@@ -202,33 +306,79 @@ __global__ __launch_bounds__(kT) void k_stats(Args a) {
     }
     const float mc = m * c;
 
+    // min-p on: only entries with e >= min_p can be kept, and every entry with
+    // a larger logit has a larger e.  One pass collects those entries (key,
+    // mass in 2^-40 units) and the row's total mass; top-p is resolved among
+    // them; the kept mass is their integer sum.
+    if (a.min_p > 0.f) {
+        if (t == 0) sh.ncand = 0;
+        __syncthreads();
+        const float minp = a.min_p;
+        unsigned long long tot = 0ull;
+        row_pass<T, VEC>(row, V, [&](float z, int64_t, bool ok) {
+            const float e = wexp(z, c, mc);
+            const unsigned long long q = ok ? (unsigned long long)(e * kFix40) : 0ull;
+            tot += q;
+            const bool in = ok && e >= minp;
+            const uint64_t mask = __ballot(in);
+            if (mask) {
+                int base = 0;
+                if (lane == 0) base = atomicAdd(&sh.ncand, __popcll(mask));
+                base = __shfl(base, 0, kWave);
+                const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
+                if (in && slot < kCand) {
+                    sh.ck[slot] = fkey(z);
+                    sh.cq[slot] = q;
+                }
+            }
+        });
+        const unsigned long long S = block_sum_u64(tot, sh);
+        const int n = sh.ncand;
+        if (n <= kCand) {
+            uint32_t tau = 0;
+            if (a.top_p < 1.f) {
+                unsigned long long cm = 0ull;
+                for (int k = t; k < n; k += kTS) cm += sh.cq[k];
+                const unsigned long long C2 = block_sum_u64(cm, sh);
+                const double need = (double)a.top_p * (double)S;
+                if ((double)C2 >= need) tau = radix_cut(sh, n, need);
+            }
+            unsigned long long kept = 0ull;
+            for (int k = t; k < n; k += kTS)
+                if (sh.ck[k] >= tau) kept += sh.cq[k];
+            const unsigned long long K2 = block_sum_u64(kept, sh);
+            if (t == 0) {
+                st.tau = tau;
+                st.s = (double)K2 / (double)kFix40;
+                a.stats[b * S2 + s] = st;
+            }
+            return;
+        }
+        // more entries pass min-p than fit: the general passes below
+    }
+
     // pass 2: top-p cut
     uint32_t tau = 0;
     if (a.top_p < 1.f) {
-        for (int k = t; k < kBins; k += kT) {
+        for (int k = t; k < kBins; k += kTS) {
             sh.hm[k] = 0ull;
             sh.hc[k] = 0u;
         }
         __syncthreads();
         unsigned long long tot = 0ull;
-        for (int64_t j = t; j < V; j += kT) {
-            const float w = __builtin_fmaf(ld(row, j), c, -mc);   // -u
-            const unsigned long long q = (unsigned long long)(hw_exp2(w) * 4294967296.f);
+        row_pass<T, VEC>(row, V, [&](float z, int64_t, bool ok) {
+            const float w = __builtin_fmaf(z, c, -mc);  // -u
+            const unsigned long long q = ok ? (unsigned long long)(hw_exp2(w) * kFix40) : 0ull;
             tot += q;
             const float u = -w;
-            if (u < 32.f && q) {
+            if (q && u < 32.f) {
                 const int bin = (int)(u * kBinScale);
                 atomicAdd(&sh.hm[bin], q);
                 atomicAdd(&sh.hc[bin], 1u);
             }
-        }
-        // the total over the workgroup (integer: exact in any order)
-        for (int o = kWave / 2; o > 0; o >>= 1) tot += __shfl_xor(tot, o, kWave);
-        if (lane == 0) sh.red_u[wv] = tot;
-        __syncthreads();
+        });
+        const unsigned long long S = block_sum_u64(tot, sh);
         if (t == 0) {
-            unsigned long long S = 0ull;
-            for (int k = 0; k < kW; ++k) S += sh.red_u[k];
             const double need = (double)a.top_p * (double)S;
             unsigned long long acc = 0ull;
             int bs = kBins - 1;
@@ -246,21 +396,15 @@ __global__ __launch_bounds__(kT) void k_stats(Args a) {
         }
         __syncthreads();
         const int bs = sh.bstar;
+        const double rem = sh.rem;
         const bool fits = sh.hc[bs] <= (uint32_t)kCand;
         // collect the crossing bin's entries (or only their smallest key)
-        for (int64_t j0 = 0; j0 < V; j0 += kT) {
-            const int64_t j = j0 + t;
-            bool in = false;
-            uint32_t key = 0;
-            unsigned long long q = 0;
-            if (j < V) {
-                const float z = ld(row, j);
-                const float w = __builtin_fmaf(z, c, -mc);
-                q = (unsigned long long)(hw_exp2(w) * 4294967296.f);
-                const float u = -w;
-                in = q && u < 32.f && (int)(u * kBinScale) == bs;
-                key = fkey(z);
-            }
+        row_pass<T, VEC>(row, V, [&](float z, int64_t, bool ok) {
+            const float w = __builtin_fmaf(z, c, -mc);
+            const unsigned long long q = ok ? (unsigned long long)(hw_exp2(w) * kFix40) : 0ull;
+            const float u = -w;
+            const bool in = q && u < 32.f && (int)(u * kBinScale) == bs;
+            const uint32_t key = fkey(z);
             if (fits) {
                 const uint64_t mask = __ballot(in);
                 if (mask) {
@@ -276,61 +420,29 @@ __global__ __launch_bounds__(kT) void k_stats(Args a) {
             } else if (in) {
                 atomicMin(&sh.kmin, key);
             }
-        }
+        });
         __syncthreads();
         if (fits) {
-            // radix select, descending: the key at which the mass reaches rem
-            const int n = sh.ncand;
-            uint32_t prefix = 0;
-            double rem = sh.rem;
-            for (int lvl = 0; lvl < 4; ++lvl) {
-                const int shift = 24 - 8 * lvl;
-                sh.dig[t] = 0ull;
-                __syncthreads();
-                for (int k = t; k < n; k += kT) {
-                    const uint32_t key = sh.ck[k];
-                    const bool match = lvl == 0 || (key >> (shift + 8)) == prefix;
-                    if (match) atomicAdd(&sh.dig[(key >> shift) & 255u], sh.cq[k]);
-                }
-                __syncthreads();
-                if (t == 0) {
-                    unsigned long long acc = 0ull;
-                    int dsel = 0;
-                    for (int dd = 255; dd >= 0; --dd) {
-                        if ((double)(acc + sh.dig[dd]) >= rem) {
-                            dsel = dd;
-                            break;
-                        }
-                        acc += sh.dig[dd];
-                    }
-                    sh.prefix = (prefix << 8) | (uint32_t)dsel;
-                    sh.rem = rem - (double)acc;
-                }
-                __syncthreads();
-                prefix = sh.prefix;
-                rem = sh.rem;
-            }
-            tau = prefix;
+            tau = radix_cut(sh, sh.ncand, rem);
         } else {
             tau = sh.kmin;
             st.coarse = 1;
         }
     }
 
-    // pass 3: kept mass
+    // pass 3: kept mass, fp64 per thread, then in thread order
     double sum = 0.0;
     const float minp = a.min_p;
-    for (int64_t j = t; j < V; j += kT) {
-        const float z = ld(row, j);
+    row_pass<T, VEC>(row, V, [&](float z, int64_t, bool ok) {
         const float e = wexp(z, c, mc);
-        if (fkey(z) >= tau && e >= minp) sum += (double)e;
-    }
+        if (ok && fkey(z) >= tau && e >= minp) sum += (double)e;
+    });
     for (int o = kWave / 2; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
     if (lane == 0) sh.red_d[wv] = sum;
     __syncthreads();
     if (t == 0) {
         double S = 0.0;
-        for (int k = 0; k < kW; ++k) S += sh.red_d[k];
+        for (int k = 0; k < kWS; ++k) S += sh.red_d[k];
         st.tau = tau;
         st.s = S;
         a.stats[b * S2 + s] = st;
@@ -354,15 +466,20 @@ __device__ __forceinline__ float kept_w(float z, float c, const Stat& st, float 
     return (fkey(z) >= st.tau && e >= minp) ? e : 0.f;
 }
 
-// draw weight of entry j: the residual after a rejection, p' for the bonus,
-// p' again (pmode 2) when the residual is empty
+// draw weight of an entry with target logit zp and draft logit zq: the
+// residual after a rejection (pmode 0), p' for the bonus (1), p' again (2)
+// when the residual is empty
+__device__ __forceinline__ float draw_wz(float zp, float zq, int pmode, const Args& a, const Stat& sp,
+                                         const Stat& sq, float invp, float invq) {
+    const float wp = kept_w(zp, a.cp, sp, a.min_p);
+    if (pmode != 0) return wp;
+    const float wq = kept_w(zq, a.cq, sq, a.min_p);
+    return fmaxf(wp * invp - wq * invq, 0.f);
+}
 template <typename T>
 __device__ __forceinline__ float draw_w(const T* zr, const T* dr, int64_t j, int pmode, const Args& a,
                                         const Stat& sp, const Stat& sq, float invp, float invq) {
-    const float wp = kept_w(ld(zr, j), a.cp, sp, a.min_p);
-    if (pmode != 0) return wp;
-    const float wq = kept_w(ld(dr, j), a.cq, sq, a.min_p);
-    return fmaxf(wp * invp - wq * invq, 0.f);
+    return draw_wz(ld(zr, j), pmode == 0 ? ld(dr, j) : 0.f, pmode, a, sp, sq, invp, invq);
 }
 
 __device__ __forceinline__ double block_sum(double v, double* sh) {
@@ -408,7 +525,30 @@ __device__ __forceinline__ void last_positive(bool pos, int base, AccShared& sh)
     __syncthreads();
 }
 
-template <typename T>
+// The EPT entries [j0, j0 + EPT) of a row, in index order (16-byte loads when
+// the rows are aligned); entries past V read as -inf (weight 0).
+template <typename T, bool VEC, int EPT>
+__device__ __forceinline__ void load_entries(const T* row, int64_t V, int64_t j0, float (&z)[EPT]) {
+    if constexpr (VEC) {
+        constexpr int W = 16 / (int)sizeof(T);
+        const uint4* p = reinterpret_cast<const uint4*>(row + j0);
+        uint4 r[EPT / W];
+#pragma unroll
+        for (int k = 0; k < EPT / W; ++k) r[k] = (j0 + (int64_t)k * W < V) ? p[k] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+        for (int k = 0; k < EPT / W; ++k) {
+            unpack_vec(r[k], z + k * W, T{});
+            if (j0 + (int64_t)k * W >= V)
+#pragma unroll
+                for (int e = 0; e < W; ++e) z[k * W + e] = -INFINITY;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) z[e] = (j0 + e < V) ? ld(row, j0 + e) : -INFINITY;
+    }
+}
+
+template <typename T, bool VEC>
 __global__ __launch_bounds__(kT) void k_accept(Args a) {
     constexpr int CH = chunk_of<T>(), EPT = ept_of<T>();
     __shared__ AccShared sh;
@@ -498,11 +638,14 @@ __global__ __launch_bounds__(kT) void k_accept(Args a) {
     const int64_t chunk0 = (int64_t)ci * CH;
     const int64_t j0 = chunk0 + (int64_t)t * EPT;
     double own = 0.0, ownp = 0.0;
-    for (int e = 0; e < EPT; ++e) {
-        const int64_t j = j0 + e;
-        if (j < V) {
-            own += (double)draw_w(zr, dr, j, reject ? 0 : 1, a, sp, sq, invp, invq);
-            if (reject) ownp += (double)kept_w(ld(zr, j), a.cp, sp, a.min_p);
+    {
+        float zz[EPT], dd[EPT];
+        load_entries<T, VEC, EPT>(zr, V, j0, zz);
+        if (reject) load_entries<T, VEC, EPT>(dr, V, j0, dd);
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+            own += (double)draw_wz(zz[e], reject ? dd[e] : 0.f, reject ? 0 : 1, a, sp, sq, invp, invq);
+            if (reject) ownp += (double)kept_w(zz[e], a.cp, sp, a.min_p);
         }
     }
     uint64_t* tsrow = a.tsum + b * a.C * kT;
@@ -574,10 +717,10 @@ __global__ __launch_bounds__(kT) void k_accept(Args a) {
     double ts;
     if (pmode == 2) {
         ts = 0.0;
-        for (int e = 0; e < EPT; ++e) {
-            const int64_t j = cb + (int64_t)t * EPT + e;
-            if (j < V) ts += (double)draw_w(zr, dr, j, 2, a, sp, sq, invp, invq);
-        }
+        float zz[EPT];
+        load_entries<T, VEC, EPT>(zr, V, cb + (int64_t)t * EPT, zz);
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) ts += (double)draw_wz(zz[e], 0.f, 2, a, sp, sq, invp, invq);
     } else {
         ts = bitsd(co_load(tsrow + (int64_t)cstar * kT + t));
     }
@@ -701,12 +844,24 @@ extern "C" int spec_accept_sampled(const void* target_logits, const void* draft_
     a.tsum = reinterpret_cast<uint64_t*>(ws + lay.tsum_off);
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     const dim3 gs((unsigned)(B * (2 * K + 1))), ga((unsigned)(B * C));
+    auto al16 = [](const void* p) { return p == nullptr || ((uintptr_t)p & 15) == 0; };
+    const bool rows_aligned = al16(target_logits) && al16(draft_logits);
     if (logits_dtype == SPEC_BF16) {
-        hipLaunchKernelGGL(k_stats<bf16_t>, gs, dim3(kT), 0, s, a);
-        hipLaunchKernelGGL(k_accept<bf16_t>, ga, dim3(kT), 0, s, a);
+        if (rows_aligned && V % 8 == 0) {
+            hipLaunchKernelGGL((k_stats<bf16_t, true>), gs, dim3(kTS), 0, s, a);
+            hipLaunchKernelGGL((k_accept<bf16_t, true>), ga, dim3(kT), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((k_stats<bf16_t, false>), gs, dim3(kTS), 0, s, a);
+            hipLaunchKernelGGL((k_accept<bf16_t, false>), ga, dim3(kT), 0, s, a);
+        }
     } else {
-        hipLaunchKernelGGL(k_stats<float>, gs, dim3(kT), 0, s, a);
-        hipLaunchKernelGGL(k_accept<float>, ga, dim3(kT), 0, s, a);
+        if (rows_aligned && V % 4 == 0) {
+            hipLaunchKernelGGL((k_stats<float, true>), gs, dim3(kTS), 0, s, a);
+            hipLaunchKernelGGL((k_accept<float, true>), ga, dim3(kT), 0, s, a);
+        } else {
+            hipLaunchKernelGGL((k_stats<float, false>), gs, dim3(kTS), 0, s, a);
+            hipLaunchKernelGGL((k_accept<float, false>), ga, dim3(kT), 0, s, a);
+        }
     }
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;
 }

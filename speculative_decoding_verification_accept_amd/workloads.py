@@ -238,3 +238,18 @@ def attention_inputs(B: int, K: int, H: int, Hkv: int, ctx_lens, S: int, seed: i
     lens = None if draft_lens is None else torch.as_tensor(np.asarray(draft_lens, dtype=np.int32),
                                                            device=device)
     return q, kc, vc, ctx, lens
+
+
+def sampled_accept_device(seed: int, device, B: int = 64, K: int = 7, V: int = 128256,
+                          noise: float = 1.5):
+    """Device-resident inputs for accept/reject with the draft as logits:
+    bf16 target logits ~ N(0, 3^2), bf16 draft logits = target + N(0, noise^2),
+    ragged L_b ~ U{1..K}; each draft token is the draft's top logit (always
+    inside the draft's filtered distribution)."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    z = (3.0 * torch.randn(B, K + 1, V, generator=g, device=device)).to(torch.bfloat16)
+    d = (z[:, :K].float() + noise * torch.randn(B, K, V, generator=g, device=device)).to(torch.bfloat16)
+    x = d.float().argmax(-1).to(torch.int32)
+    L = torch.randint(1, K + 1, (B,), generator=g, device=device, dtype=torch.int32)
+    return z, d, x, L
