@@ -336,6 +336,72 @@ def bench_control(torch, sv, sweep, reps=200):
     return out
 
 
+def _timed(fn, budget_s):
+    """Runs fn repeatedly for about budget_s (at least once): seconds per run."""
+    n, t0 = 0, time.perf_counter()
+    while n == 0 or time.perf_counter() - t0 < budget_s:
+        fn()
+        n += 1
+    return (time.perf_counter() - t0) / n, n
+
+
+def _cpu_rows(workloads, cores, budget_s=2.0):
+    """The oracle, as it stands, on a bounded sample of each other measured
+    path, scaled to that path's unit: the figures the GPU paths are set
+    against in the breakdown."""
+    import numpy as np
+
+    import oracle
+    from oracle import attention as A
+    from oracle import control as C
+    from oracle import sampled as S
+    out = {}
+    # accept/reject at scale (8 of the 64 rows; positions = sum(L_b + 1))
+    inp = workloads.accept_inputs(8, 7, 128256, logit_std=3.0, draft_noise=1.5, temperature=0.8,
+                                  seed=3, bf16=True, ragged=True)
+    z = inp.logits_f32()
+    pos = int((inp.draft_lens + 1).sum())
+    sec, n = _timed(lambda: oracle.spec_accept(z, inp.draft_probs, inp.draft_tokens, inp.draft_lens,
+                                                0.8, 77, 0, nthreads=cores), budget_s)
+    out["accept_at_scale"] = dict(value=round(pos / sec, 1), unit="verified positions/s",
+                                  sample=f"8 rows of B=64 K=7 V=128256, {n} run(s), {cores} threads")
+    # the sampler-filter path (2 rows)
+    zs = z[:2]
+    ds = (zs[:, :7] + np.random.default_rng(4).normal(0, 1.5, zs[:, :7].shape)).astype(np.float32)
+    xs = ds.argmax(-1).astype(np.int32)
+    Ls = inp.draft_lens[:2]
+    sec, n = _timed(lambda: S.spec_accept_sampled(zs, ds, xs, Ls, 0.8, 0.8, 0.95, 0.05, 77, 0),
+                    budget_s)
+    out["accept_sampled_at_scale"] = dict(
+        value=round(int((Ls + 1).sum()) / sec, 1), unit="verified positions/s",
+        sample=f"2 rows of B=64 K=7 V=128256 with top-p 0.95, min-p 0.05, {n} run(s), 1 thread")
+    # verify GEMM, M = 32 (fp64 matmul on an eighth of the columns, scaled)
+    X = np.random.default_rng(5).normal(size=(32, 4096)).astype(np.float32)
+    W = np.random.default_rng(6).normal(0, 0.02, size=(4096, 1792)).astype(np.float32)
+    sec, n = _timed(lambda: oracle.verify_linear(X, W), budget_s)
+    out["gemm_M32"] = dict(value=round(2 * 32 * 4096 * 1792 / sec * 1e-9, 2), unit="GFLOP/s",
+                           sample=f"X[32,4096] x W[4096,1792] fp64, {n} run(s)")
+    # verify attention: one query row against an 8192-token cache, scaled
+    # to the 8 x 8192 grouped-head call at D = 7 (8 x 8 x 32 rows)
+    rng = np.random.default_rng(7)
+    q = rng.normal(size=(1, 8, 32, 128)).astype(np.float32)
+    kc = rng.normal(size=(1, 8, 8200, 128)).astype(np.float32)
+    vc = rng.normal(size=(1, 8, 8200, 128)).astype(np.float32)
+    sec, n = _timed(lambda: A.verify_attention_row(q, kc, vc, 8192, 0, 7, 5, 128 ** -0.5), budget_s)
+    out["verify_attention"] = dict(value=round(sec * 8 * 8 * 32 * 1e6, 1), unit="us per call",
+                                   sample=f"one row of 8 x 8192 grouped-head D=7 scaled x2048, {n} run(s)")
+    # depth controller, B = 4096
+    rngc = np.random.default_rng(8)
+    Lc = rngc.integers(1, 8, 4096)
+    ac = np.floor(rngc.random(4096) * (Lc + 1)).astype(np.int64)
+    stc, tel = C.new_state(4096), C.new_telemetry()
+    sec, n = _timed(lambda: C.adapt(ac, Lc, 7, stc, tel, k_min=1, k_max=7, window=8, policy=1,
+                                    draft_cost=0.05), budget_s)
+    out["adapt_B4096"] = dict(value=round(sec * 1e6, 1), unit="us per call",
+                              sample=f"B=4096 K=7, {n} run(s), 1 thread")
+    return out
+
+
 def cpu_baseline(torch, workloads, st, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the step: the fp64
     GEMM reference on a column slice of the lm-head (scaled to all columns)
@@ -370,7 +436,8 @@ def cpu_baseline(torch, workloads, st, budget_s=12.0):
         t_acc += t2 - t1
         n += 1
     per_step = (t_gemm + t_acc) / n
-    return dict(value=round(B * (K + 1) / per_step, 2), unit="verified positions/s",
+    rows = _cpu_rows(workloads, cores)
+    return dict(value=round(B * (K + 1) / per_step, 2), unit="verified positions/s", paths=rows,
                 cores=max(cores, blas_threads), kind="oracle",
                 sample=(f"{n} step(s): fp64 numpy GEMM on {ncols} of {V} lm-head columns scaled "
                         f"x{V / ncols:.0f} ({t_gemm / n:.2f} s/step) + fp64 C accept oracle on all "
