@@ -211,6 +211,48 @@ __device__ __forceinline__ void row_pass(const T* row, int64_t V, F&& f) {
 // Radix select, descending, over the n collected entries (keys sh.ck, masses
 // sh.cq): the key at which the mass, counted from the largest key down and
 // taking equal keys together, first reaches rem.  Four 8-bit digits.
+// One digit of the radix top-p cut.  dig[] holds the 2^-40 masses of the 256
+// digit values at this level; the cut digit is the largest d whose mass at or
+// above d reaches rem.  Threads 0..255 hold one digit each; suffix sums in
+// waves, then across waves, and a ballot counts the digits that reach rem
+// (a prefix of 0..255, as the suffix sums only grow towards digit 0).  The
+// thread holding the cut digit writes the extended prefix and rem less the
+// mass strictly above the cut; with no such digit (rounding), digit 0 and
+// rem less the whole mass.  Every thread of the block calls it; wtot and wcnt
+// hold 256 / 64 entries.
+__device__ __forceinline__ void pick_digit(const unsigned long long* dig, double rem, uint32_t prefix,
+                                           unsigned long long* wtot, int* wcnt, uint32_t* out_prefix,
+                                           double* out_rem) {
+    constexpr int kDW = 256 / kWave;
+    const int t = threadIdx.x, lane = t & (kWave - 1), wv = t / kWave;
+    unsigned long long x = 0ull, v = 0ull;
+    if (t < 256) {
+        v = dig[t];
+        x = v;
+        for (int o = 1; o < kWave; o <<= 1) {
+            const unsigned long long n = __shfl_down(x, o, kWave);
+            if (lane + o < kWave) x += n;
+        }
+        if (lane == 0) wtot[wv] = x;
+    }
+    __syncthreads();
+    bool f = false;
+    if (t < 256) {
+        for (int k = wv + 1; k < kDW; ++k) x += wtot[k];
+        f = (double)x >= rem;
+    }
+    const unsigned long long bal = __ballot(f);
+    if (t < 256 && lane == 0) wcnt[wv] = __popcll(bal);
+    __syncthreads();
+    int cnt = 0;
+    for (int k = 0; k < kDW; ++k) cnt += wcnt[k];
+    const int w = cnt > 0 ? cnt - 1 : 0;
+    if (t == w) {
+        *out_prefix = (prefix << 8) | (uint32_t)w;
+        *out_rem = rem - (double)(cnt > 0 ? x - v : x);
+    }
+}
+
 __device__ __forceinline__ uint32_t radix_cut(StatShared& sh, int n, double rem) {
     const int t = threadIdx.x;
     uint32_t prefix = 0;
@@ -223,19 +265,7 @@ __device__ __forceinline__ uint32_t radix_cut(StatShared& sh, int n, double rem)
             if (lvl == 0 || (key >> (shift + 8)) == prefix) atomicAdd(&sh.dig[(key >> shift) & 255u], sh.cq[k]);
         }
         __syncthreads();
-        if (t == 0) {
-            unsigned long long acc = 0ull;
-            int dsel = 0;
-            for (int dd = 255; dd >= 0; --dd) {
-                if ((double)(acc + sh.dig[dd]) >= rem) {
-                    dsel = dd;
-                    break;
-                }
-                acc += sh.dig[dd];
-            }
-            sh.prefix = (prefix << 8) | (uint32_t)dsel;
-            sh.rem = rem - (double)acc;
-        }
+        pick_digit(sh.dig, rem, prefix, sh.red_u, sh.red_i, &sh.prefix, &sh.rem);
         __syncthreads();
         prefix = sh.prefix;
         rem = sh.rem;
