@@ -34,11 +34,16 @@
 //            Pass 3: the kept mass S' = sum of kept e in fp64, in a fixed
 //            order.  A crossing bin of more than 4096 entries keeps the
 //            whole bin and sets SPEC_ROW_FILTER_COARSE.
-//            With min-p on, pass 2 instead collects the entries that pass
-//            min-p (every larger logit passes too), with the row's total
-//            mass; top-p is resolved among them by the same radix select and
-//            S' is their integer kept sum: two passes, unless more than 4096
-//            entries pass min-p (then the general passes run).
+//            With min-p on, one pass instead: the max, the total mass (each
+//            thread's fp64 sum relative to a power of two at least its
+//            reference max, rescaled exactly as the reference grows; the
+//            reference follows the workgroup's running max in LDS), and the
+//            entries that can pass min-p against that running max (a superset
+//            of those passing against m).  Once m is known their masses are
+//            computed in 2^-40 units, top-p is resolved among them by the same
+//            radix select (every larger logit passes min-p too), and S' is
+//            their integer kept sum.  More than 4096 collected entries: the
+//            general passes run.
 //  k_accept  one workgroup per (row, chunk of 16 KB of logits).  Every
 //            workgroup computes the row's decision itself from the stats and
 //            two gathers per position (p'(x_i), q'(x_i) in fp64, the same
@@ -50,6 +55,8 @@
 //            Exchange between workgroups uses agent-scope atomic accesses
 //            (SC1) and a drain of the workgroup's stores before it counts in.
 #include <math.h>
+
+#include <type_traits>
 
 #include "device_common.hpp"
 #include "philox.hpp"
@@ -105,6 +112,10 @@ __device__ __forceinline__ uint32_t fkey(float z) {
     const uint32_t u = __float_as_uint(z == 0.f ? 0.f : z);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+// the value of a key (+0 for the shared zero key)
+__device__ __forceinline__ float funkey(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
 
 // weight of logit z relative to the row max: 2^(fl(z c - fl(m c)))
 __device__ __forceinline__ float wexp(float z, float c, float mc) { return hw_exp2(__builtin_fmaf(z, c, -mc)); }
@@ -143,21 +154,27 @@ __device__ __forceinline__ int row_len(const Args& a, int64_t b) { return a.lens
 // ---- k_stats ----------------------------------------------------------------------------------
 constexpr int kTS = 512;                    // threads of a statistics workgroup
 constexpr int kWS = kTS / kWave;
-constexpr int kU = 4;                       // 16-byte loads per thread in flight per round
+constexpr int kU = 2;                       // 16-byte loads per thread per round
 constexpr float kFix40 = 1099511627776.f;   // 2^40: fixed-point unit of the mass histograms
 
 struct StatShared {
-    unsigned long long hm[kBins];
-    uint32_t hc[kBins];
-    uint32_t ck[kCand];
-    unsigned long long cq[kCand];
+    union {
+        struct {  // coarse histogram of the top-p pass
+            unsigned long long hm[kBins];
+            uint32_t hc[kBins];
+        };
+        struct {  // collected entries: key, mass in 2^-40 units
+            uint32_t ck[kCand];
+            unsigned long long cq[kCand];
+        };
+    };
     unsigned long long dig[256];
     unsigned long long red_u[kWS];
     double red_d[kWS];
     float red_f[kWS];
     int red_i[kWS];
     int ncand, bstar;
-    uint32_t prefix, kmin;
+    uint32_t prefix, kmin, mrun;
     double rem;
 };
 
@@ -171,7 +188,7 @@ __device__ __forceinline__ void unpack_vec(const uint4& r, float* z, float) {
 }
 
 // Calls f(z, j, valid) for every entry j of a row, in rounds of kU loads per
-// thread issued before use.  Every thread runs the same rounds and the same
+// thread; a round's loads go out before the previous round is used.  Every thread runs the same rounds and the same
 // calls (valid is false past the row): f may use wave-wide operations.
 // Loads past the end re-read the last in-range vector instead of branching.
 template <typename T, bool VEC, typename F>
@@ -181,10 +198,14 @@ __device__ __forceinline__ void row_pass(const T* row, int64_t V, F&& f) {
         constexpr int W = 16 / (int)sizeof(T);
         const int64_t nv = V / W;
         const uint4* p = reinterpret_cast<const uint4*>(row);
-        for (int64_t v0 = 0; v0 < nv; v0 += (int64_t)kTS * kU) {
-            uint4 r[kU];
+        constexpr int64_t kStep = (int64_t)kTS * kU;
+        // the next round's loads go out before this round is consumed
+        uint4 r[kU], nr[kU];
 #pragma unroll
-            for (int u = 0; u < kU; ++u) r[u] = p[min(v0 + (int64_t)u * kTS + t, nv - 1)];
+        for (int u = 0; u < kU; ++u) r[u] = p[min((int64_t)u * kTS + t, nv - 1)];
+        for (int64_t v0 = 0; v0 < nv; v0 += kStep) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) nr[u] = p[min(v0 + kStep + (int64_t)u * kTS + t, nv - 1)];
 #pragma unroll
             for (int u = 0; u < kU; ++u) {
                 const int64_t v = v0 + (int64_t)u * kTS + t;
@@ -193,6 +214,8 @@ __device__ __forceinline__ void row_pass(const T* row, int64_t V, F&& f) {
 #pragma unroll
                 for (int k = 0; k < W; ++k) f(z[k], v * W + k, v < nv);
             }
+#pragma unroll
+            for (int u = 0; u < kU; ++u) r[u] = nr[u];
         }
     } else {
         for (int64_t j0 = 0; j0 < V; j0 += (int64_t)kTS * kU) {
@@ -204,6 +227,78 @@ __device__ __forceinline__ void row_pass(const T* row, int64_t V, F&& f) {
                 const int64_t j = j0 + (int64_t)u * kTS + t;
                 f(z[u], j, j < V);
             }
+        }
+    }
+}
+
+// One round of a thread's entries: kU 16-byte loads, unpacked on each use
+// (a bf16 entry is one shift or mask), so the round costs 4 kU registers
+// whatever the dtype.
+template <typename T>
+struct VecRound {
+    static constexpr int W = 16 / (int)sizeof(T);
+    static constexpr int N = kU * W;
+    uint4 r[kU];
+    __device__ __forceinline__ float operator[](int e) const {
+        const uint4& v = r[e / W];
+        const int k = sizeof(T) == 2 ? (e % W) >> 1 : e % W;
+        const uint32_t w = k == 0 ? v.x : k == 1 ? v.y : k == 2 ? v.z : v.w;
+        if constexpr (sizeof(T) == 2) return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+        else return __uint_as_float(w);
+    }
+    // an opaque copy: its entries are unpacked anew where they are used, so
+    // values unpacked earlier need not stay live in registers
+    __device__ __forceinline__ VecRound fresh() const {
+        VecRound c = *this;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) asm volatile("" : "+v"(c.r[u].x), "+v"(c.r[u].y), "+v"(c.r[u].z), "+v"(c.r[u].w));
+        return c;
+    }
+};
+struct ScalarRound {
+    static constexpr int N = kU;
+    float z[kU];
+    __device__ __forceinline__ float operator[](int e) const { return z[e]; }
+    __device__ __forceinline__ ScalarRound fresh() const { return *this; }
+};
+
+// Calls f(z, ok) once per round with this thread's entries of the round
+// (z[e], e < N, N / kU per load) and a bit mask of its loads (bit u for
+// entries u N / kU .. (u + 1) N / kU - 1) that lie inside the row.  Every
+// thread runs the same rounds.
+template <typename T, bool VEC, typename F>
+__device__ __forceinline__ void row_rounds(const T* row, int64_t V, F&& f) {
+    const int t = threadIdx.x;
+    if constexpr (VEC) {
+        constexpr int W = VecRound<T>::W;
+        const int64_t nv = V / W;
+        const uint4* p = reinterpret_cast<const uint4*>(row);
+        constexpr int64_t kStep = (int64_t)kTS * kU;
+        // the next round's loads go out before this round is consumed
+        // (clamped addresses: past the row they read its last vector again)
+        VecRound<T> z, nz;
+#pragma unroll
+        for (int u = 0; u < kU; ++u) z.r[u] = p[min((int64_t)u * kTS + t, nv - 1)];
+        for (int64_t v0 = 0; v0 < nv; v0 += kStep) {
+#pragma unroll
+            for (int u = 0; u < kU; ++u) nz.r[u] = p[min(v0 + kStep + (int64_t)u * kTS + t, nv - 1)];
+            uint32_t ok = 0u;
+#pragma unroll
+            for (int u = 0; u < kU; ++u)
+                if (v0 + (int64_t)u * kTS + t < nv) ok |= 1u << u;
+            f(z, ok);
+            z = nz;
+        }
+    } else {
+        for (int64_t j0 = 0; j0 < V; j0 += (int64_t)kTS * kU) {
+            ScalarRound z;
+            uint32_t ok = 0u;
+#pragma unroll
+            for (int u = 0; u < kU; ++u) {
+                z.z[u] = ld(row, min(j0 + (int64_t)u * kTS + t, V - 1));
+                if (j0 + (int64_t)u * kTS + t < V) ok |= 1u << u;
+            }
+            f(z, ok);
         }
     }
 }
@@ -286,6 +381,18 @@ __device__ __forceinline__ unsigned long long block_sum_u64(unsigned long long v
     return r;
 }
 
+__device__ __forceinline__ double block_sum_d(double v, StatShared& sh) {
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    __syncthreads();
+    if (lane == 0) sh.red_d[wv] = v;
+    __syncthreads();
+    double r = 0.0;
+    for (int k = 0; k < kWS; ++k) r += sh.red_d[k];
+    __syncthreads();
+    return r;
+}
+
 template <typename T, bool VEC>
 __global__ __launch_bounds__(kTS) void k_stats(Args a) {
     __shared__ StatShared sh;
@@ -302,17 +409,132 @@ __global__ __launch_bounds__(kTS) void k_stats(Args a) {
     const T* row = draft ? static_cast<const T*>(a.d) + (b * a.K + pos) * V
                          : static_cast<const T*>(a.z) + (b * (a.K + 1) + pos) * V;
     const float c = draft ? a.cq : a.cp;
+    const float minp = a.min_p;
     Stat st{};
 
-    // pass 1: max, non-finite flag
     float mx = -INFINITY;
     int bad = 0;
-    row_pass<T, VEC>(row, V, [&](float z, int64_t, bool ok) {
-        if (ok) {
-            bad |= (z != z) | (z == INFINITY);
-            mx = fmaxf(mx, z);
+    double sacc = 0.0;   // min-p pass: this thread's mass relative to 2^(mcref)
+    float mcref = 0.f;
+    if (minp > 0.f) {
+        // One pass: max, non-finite flag, total mass, and the entries that
+        // can pass min-p.  Each thread sums its mass relative to 2^kref, kref
+        // an integer at least its reference max times c (the reference: its
+        // own max so far, raised to the workgroup's running max), so a
+        // growing reference rescales the sum exactly by a power of two.  A
+        // round is summed against the reference from before it (its entries
+        // are unpacked once and used at once); a round whose max lies more
+        // than 2^64 above that reference, or that comes before any finite
+        // reference, is summed again against the new one.  A NaN entry
+        // makes the sum NaN.  An entry can pass min-p against the row max m
+        // only if fl(z c - fl(r c)) >= log2(min_p) for any r <= m (fl is
+        // monotone); the margin of 1e-4 covers the rounding of the exp2, of
+        // log2(min_p) and of the shift to kref.  The collected set is a
+        // superset of the entries that pass; their masses are computed once
+        // m is known.
+        if (t == 0) {
+            sh.ncand = 0;
+            sh.mrun = fkey(-INFINITY);
         }
-    });
+        __syncthreads();
+        const float lt = log2f(minp) - 1e-4f;
+        float ltr = 0.f;  // lt + fl(ref c) - kref
+        float gl = -INFINITY;
+        row_rounds<T, VEC>(row, V, [&](const auto& z, uint32_t ok) {
+            constexpr int N = std::remove_reference_t<decltype(z)>::N;
+            constexpr int G = N / kU;
+            static_assert(N <= 64, "one candidate bit per entry of the round");
+            static_assert((kU & (kU - 1)) == 0 && (G & (G - 1)) == 0, "pairwise sums over powers of two");
+            // the round's mass against 2^kr (pairwise in fp32 within each
+            // load's entries and across the loads, a fixed order) and its max
+            auto round_sum = [&](const auto& zz, float kr, float* rmax) {
+                float part[kU];
+                float rm = -INFINITY;
+#pragma unroll
+                for (int u = 0; u < kU; ++u) {
+                    float ev[G];
+                    float ru = -INFINITY;
+#pragma unroll
+                    for (int k = 0; k < G; ++k) {
+                        const float v = zz[u * G + k];
+                        ru = fmaxf(ru, v);
+                        ev[k] = hw_exp2(__builtin_fmaf(v, c, -kr));
+                    }
+#pragma unroll
+                    for (int h = G / 2; h >= 1; h /= 2)
+#pragma unroll
+                        for (int k = 0; k < h; ++k) ev[k] = ev[k] + ev[k + h];
+                    const bool valid = (ok >> u) & 1u;
+                    part[u] = valid ? ev[0] : 0.f;
+                    rm = valid ? fmaxf(rm, ru) : rm;
+                }
+#pragma unroll
+                for (int h = kU / 2; h >= 1; h /= 2)
+#pragma unroll
+                    for (int k = 0; k < h; ++k) part[k] = part[k] + part[k + h];
+                if (rmax) *rmax = rm;
+                return part[0];
+            };
+            float r;
+            const float part = round_sum(z, mcref, &r);
+            bad |= r == INFINITY;
+            if (r > gl) atomicMax(&sh.mrun, fkey(r));
+            const float g = funkey(__hip_atomic_load(&sh.mrun, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+            gl = g;
+            const bool redo = !(mx > -INFINITY) || __builtin_fmaf(r, c, -mcref) > 64.f;
+            const float nref = fmaxf(fmaxf(mx, r), g);
+            if (nref > mx && nref < INFINITY) {
+                const float nmc = nref * c;
+                const float kr = ceilf(nmc);
+                if (!redo) sacc += (double)part;
+                sacc = ldexp(sacc, (int)(mcref - kr));
+                mx = nref;
+                mcref = kr;
+                ltr = lt + (nmc - kr);
+                if (redo) sacc += (double)round_sum(z.fresh(), mcref, nullptr);
+            } else {
+                sacc += (double)part;
+            }
+            // candidates (rare after the first rounds): an entry passes the
+            // test only if the round's max does (c > 0); one LDS atomic per
+            // wave, slots in lane order
+            const bool hit = mx > -INFINITY && __builtin_fmaf(r, c, -mcref) >= ltr;
+            if (__ballot(hit)) {
+                const auto zc = z.fresh();
+                uint64_t in = 0ull;
+                if (hit) {
+#pragma unroll
+                    for (int e = 0; e < N; ++e)
+                        in |= (((ok >> (e / G)) & 1u) && __builtin_fmaf(zc[e], c, -mcref) >= ltr ? 1ull : 0ull) << e;
+                }
+                const int mine = __popcll(in);
+                int incl = mine;
+                for (int o = 1; o < kWave; o <<= 1) {
+                    const int nb = __shfl_up(incl, o, kWave);
+                    if (lane >= o) incl += nb;
+                }
+                int base = 0;
+                if (lane == kWave - 1) base = atomicAdd(&sh.ncand, incl);
+                base = __shfl(base, kWave - 1, kWave);
+                int slot = base + incl - mine;
+#pragma unroll
+                for (int e = 0; e < N; ++e)
+                    if ((in >> e) & 1ull) {
+                        if (slot < kCand) sh.ck[slot] = fkey(zc[e]);
+                        ++slot;
+                    }
+            }
+        });
+    } else {
+        // pass 1: max, non-finite flag
+        row_pass<T, VEC>(row, V, [&](float z, int64_t, bool ok) {
+            if (ok) {
+                bad |= (z != z) | (z == INFINITY);
+                mx = fmaxf(mx, z);
+            }
+        });
+    }
+    const float mthread = mx;
     mx = wave_max(mx);
     bad = wave_or(bad);
     if (lane == 0) {
@@ -336,41 +558,31 @@ __global__ __launch_bounds__(kTS) void k_stats(Args a) {
     }
     const float mc = m * c;
 
-    // min-p on: only entries with e >= min_p can be kept, and every entry with
-    // a larger logit has a larger e.  One pass collects those entries (key,
-    // mass in 2^-40 units) and the row's total mass; top-p is resolved among
-    // them; the kept mass is their integer sum.
-    if (a.min_p > 0.f) {
-        if (t == 0) sh.ncand = 0;
-        __syncthreads();
-        const float minp = a.min_p;
-        unsigned long long tot = 0ull;
-        row_pass<T, VEC>(row, V, [&](float z, int64_t, bool ok) {
-            const float e = wexp(z, c, mc);
-            const unsigned long long q = ok ? (unsigned long long)(e * kFix40) : 0ull;
-            tot += q;
-            const bool in = ok && e >= minp;
-            const uint64_t mask = __ballot(in);
-            if (mask) {
-                int base = 0;
-                if (lane == 0) base = atomicAdd(&sh.ncand, __popcll(mask));
-                base = __shfl(base, 0, kWave);
-                const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
-                if (in && slot < kCand) {
-                    sh.ck[slot] = fkey(z);
-                    sh.cq[slot] = q;
-                }
+    // min-p on: every entry with a larger logit has a larger e, so top-p is
+    // resolved exactly among the collected entries (key, mass in 2^-40
+    // units); the kept mass is their integer sum.
+    if (minp > 0.f) {
+        const double S = block_sum_d(mthread != -INFINITY && sacc != 0.0 ? sacc * exp2((double)mcref - (double)mc) : 0.0, sh);
+        if (!(S < INFINITY)) {  // a NaN entry
+            if (t == 0) {
+                st.flag = 1;
+                a.stats[b * S2 + s] = st;
             }
-        });
-        const unsigned long long S = block_sum_u64(tot, sh);
+            return;
+        }
         const int n = sh.ncand;
         if (n <= kCand) {
+            for (int k = t; k < n; k += kTS) {
+                const float e = wexp(funkey(sh.ck[k]), c, mc);
+                sh.cq[k] = e >= minp ? (unsigned long long)(e * kFix40) : 0ull;
+            }
+            __syncthreads();
             uint32_t tau = 0;
             if (a.top_p < 1.f) {
                 unsigned long long cm = 0ull;
                 for (int k = t; k < n; k += kTS) cm += sh.cq[k];
                 const unsigned long long C2 = block_sum_u64(cm, sh);
-                const double need = (double)a.top_p * (double)S;
+                const double need = (double)a.top_p * S * (double)kFix40;
                 if ((double)C2 >= need) tau = radix_cut(sh, n, need);
             }
             unsigned long long kept = 0ull;
@@ -428,6 +640,7 @@ __global__ __launch_bounds__(kTS) void k_stats(Args a) {
         const int bs = sh.bstar;
         const double rem = sh.rem;
         const bool fits = sh.hc[bs] <= (uint32_t)kCand;
+        __syncthreads();  // the entries below overwrite the histogram
         // collect the crossing bin's entries (or only their smallest key)
         row_pass<T, VEC>(row, V, [&](float z, int64_t, bool ok) {
             const float w = __builtin_fmaf(z, c, -mc);
@@ -462,7 +675,6 @@ __global__ __launch_bounds__(kTS) void k_stats(Args a) {
 
     // pass 3: kept mass, fp64 per thread, then in thread order
     double sum = 0.0;
-    const float minp = a.min_p;
     row_pass<T, VEC>(row, V, [&](float z, int64_t, bool ok) {
         const float e = wexp(z, c, mc);
         if (ok && fkey(z) >= tau && e >= minp) sum += (double)e;

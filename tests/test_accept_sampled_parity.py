@@ -135,6 +135,63 @@ def test_different_draft_temperature_and_edges():
         compare(g, o, ("edge", B, K, V), max_near=0.5)
 
 
+def _single_pass_rows(V, K, rng):
+    """Rows that stress the one-pass statistics with min-p on: a rising ramp
+    (the reference max grows every round), a jump of 600 mid-row (the round
+    is summed again against the new reference), a -inf prefix (no finite
+    reference for several rounds), a row that is -inf but for its last
+    entries, flat logits (every entry passes min-p: more entries than the
+    collection holds, so the general passes run), a NaN inside a -inf
+    prefix, a +inf mid-row, and a plain Gaussian row."""
+    B = 8
+    z = rng.normal(0, 2.0, (B, K + 1, V))
+    z[0] = np.linspace(-5.0, 30.0, V) + rng.normal(0, 0.1, (K + 1, V))
+    z[1, :, : V // 2] = rng.normal(-600.0, 1.0, (K + 1, V // 2))
+    z[2, :, : (2 * V) // 5] = -np.inf
+    z[3, :, :-5] = -np.inf
+    z[4] = rng.normal(0, 0.001, (K + 1, V))
+    z[5, :, : V // 4] = -np.inf
+    z[5, 0, 10] = np.nan
+    z[6, K, V // 2] = np.inf
+    z = z.astype(np.float32)
+    d = z[:, :K].copy()
+    fin = np.isfinite(d)
+    d[fin] += rng.normal(0, 0.5, int(fin.sum())).astype(np.float32)
+    return z, d
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("top_p", [1.0, 0.9])
+def test_min_p_one_pass_edges(bf16, top_p):
+    V, K, T, mp = 20000 + (3 if not bf16 else 0), 2, 0.8, 0.05
+    rng = np.random.default_rng(41 + bf16)
+    z, d = _single_pass_rows(V, K, rng)
+    if bf16:
+        z = torch.from_numpy(z).to(torch.bfloat16).float().numpy()
+        d = torch.from_numpy(d).to(torch.bfloat16).float().numpy()
+    if top_p < 1.0:
+        # flat logits under a top-p cut keep a crossing bin wider than the
+        # exact collection (the coarse fall-back): leave that row plain
+        z[4] = rng.normal(0, 2.0, (K + 1, V)).astype(np.float32)
+        d[4] = z[4, :K] + rng.normal(0, 0.5, (K, V)).astype(np.float32)
+        if bf16:
+            z[4] = torch.from_numpy(z[4]).to(torch.bfloat16).float().numpy()
+            d[4] = torch.from_numpy(d[4]).to(torch.bfloat16).float().numpy()
+    B = z.shape[0]
+    x = np.zeros((B, K), np.int32)
+    for b in range(B):
+        for i in range(K):
+            q = S.filtered(d[b, i], T, float(np.float32(top_p)), float(np.float32(mp)))[0]
+            if q is not None:
+                x[b, i] = rng.choice(V, p=q / q.sum())
+    g, o = run(z, d, x, np.full(B, K, np.int32), T=T, top_p=top_p, min_p=mp, seed=5, offset=1, bf16=bf16,
+               label=f"one-pass edges top_p={top_p}")
+    assert o["status"][5] == S.ROW_NONFINITE and o["status"][6] == S.ROW_NONFINITE
+    assert (g["status"][5] & S.ROW_NONFINITE) and (g["status"][6] & S.ROW_NONFINITE)
+    assert not np.any(o["status"][[0, 1, 2, 3, 4, 7]])
+    compare(g, o, ("one-pass edges", bf16, top_p), max_near=0.5)
+
+
 def test_status_bits():
     z, d, x, L = make_inputs(8, 3, 9000, std=2.0, noise=1.0, T=1.0, top_p=0.95, min_p=0.05, seed=8)
     z[0, 1, 17] = np.nan
