@@ -478,6 +478,35 @@ struct DmaCfg {
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
+// Reads of register v from lane l ^ 1 and l ^ 2 of the same quad (DPP quad
+// permutations 1,0,3,2 and 2,3,0,1).
+__device__ __forceinline__ float quad_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+// 4 x 4 transpose inside each quad of lanes: lane i (qi = lane & 3) holds
+// column i of a block in v[0..3] (v[r] = row r) and ends holding row i
+// (v[c] = column c).  Two exchanges: across lane bit 0 the registers whose
+// bit 0 differs from the lane's, then across lane bit 1 likewise.  Every
+// lane of the wave must take part.
+__device__ __forceinline__ void quad_transpose(float (&v)[4], int qi) {
+    const bool b0 = qi & 1, b1 = (qi & 2) != 0;
+    const float r01 = quad_xor1(b0 ? v[0] : v[1]);
+    const float r23 = quad_xor1(b0 ? v[2] : v[3]);
+    v[0] = b0 ? r01 : v[0];
+    v[1] = b0 ? v[1] : r01;
+    v[2] = b0 ? r23 : v[2];
+    v[3] = b0 ? v[3] : r23;
+    const float r02 = quad_xor2(b1 ? v[0] : v[2]);
+    const float r13 = quad_xor2(b1 ? v[1] : v[3]);
+    v[0] = b1 ? r02 : v[0];
+    v[2] = b1 ? v[2] : r02;
+    v[1] = b1 ? r13 : v[1];
+    v[3] = b1 ? v[3] : r13;
+}
+
 // Physical 16-byte group of logical group g in X row r (BK = 32: 4 groups of
 // 64-byte rows; BK = 64: 8 groups of 128-byte rows), and in W row kr.
 template <int XG>
@@ -675,23 +704,36 @@ __global__ __launch_bounds__(Cfg::NT) void k_dma(const uint16_t* __restrict__ X,
     for (int64_t base = st0; base < st1; base += Cfg::S)
         dma_round<Cfg>(A, wave, base, st1, aoff, boff, acc, std::make_integer_sequence<int, Cfg::S>{});
 
-    const int l32 = lane & 31, g = lane >> 5;
+    // Stores of 4 consecutive columns per lane: registers 4 jj .. 4 jj + 3
+    // of the lanes of a quad form a 4 x 4 block (lane i: column i, register
+    // r: row r); transposed inside the quad, lane i holds row i, so one
+    // 16-byte store (8 for bf16) replaces four 4-byte ones.  N is a multiple
+    // of 8 and a quad's columns start at a multiple of 4: all four are in
+    // range or none.
+    const int g = lane >> 5, qi = lane & 3, q = (lane & 31) >> 2;
     const int64_t nbase = ntile0 * Cfg::BN;
     float* dstp = splits > 1 ? partial + (int64_t)split * M * NP : nullptr;
 #pragma unroll
     for (int fm = 0; fm < Cfg::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < Cfg::FN; ++fn) {
-            const int64_t n = n0 + wn * Cfg::WN + 32 * fn + l32;
-            if (n >= N) continue;
+            const int64_t n = n0 + wn * Cfg::WN + 32 * fn + 4 * q;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int64_t m = m0 + wm * Cfg::WM + 32 * fm + 8 * (j / 4) + 4 * g + (j % 4);
-                if (m >= M) continue;
-                const float v = acc[fm][fn][j];
-                if (dstp) dstp[m * NP + n - nbase] = v;
-                else if (y_bf16) static_cast<uint16_t*>(Y)[m * N + n] = f32_to_bf16(v);
-                else static_cast<float*>(Y)[m * N + n] = v;
+            for (int jj = 0; jj < 4; ++jj) {
+                float v[4] = {acc[fm][fn][4 * jj], acc[fm][fn][4 * jj + 1], acc[fm][fn][4 * jj + 2],
+                              acc[fm][fn][4 * jj + 3]};
+                quad_transpose(v, qi);
+                const int64_t m = m0 + wm * Cfg::WM + 32 * fm + 8 * jj + 4 * g + qi;
+                if (m >= M || n >= N) continue;
+                if (dstp) {
+                    *reinterpret_cast<float4*>(dstp + m * NP + n - nbase) = make_float4(v[0], v[1], v[2], v[3]);
+                } else if (y_bf16) {
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + m * N + n) =
+                        make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                                   (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+                } else {
+                    *reinterpret_cast<float4*>(static_cast<float*>(Y) + m * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+                }
             }
         }
 }
