@@ -107,6 +107,29 @@ def test_at_scale_vocab_bf16():
     print(compare(g, o, "scale"))
 
 
+def test_bench_size_sampled_rows():
+    # the benchmark's launch: B = 64, K = 7, V = 128256 bf16, T = 0.8, top-p
+    # 0.95, min-p 0.05, its own input recipe; the rows are independent (the
+    # Philox stream of row b is that of global row b), so the oracle checks a
+    # sample of them one by one with row_base = b
+    from speculative_decoding_verification_accept_amd import workloads
+    dev = torch.device("cuda:0")
+    z, d, x, L = workloads.sampled_accept_device(4000, dev)
+    B, K1, V = z.shape
+    print(f"[spec_accept_sampled] bench size B={B} K={K1 - 1} V={V}", flush=True)
+    res = sv.accept_sampled(z, d, x, L, temperature=0.8, top_p=0.95, min_p=0.05, seed=77, offset=0)
+    torch.cuda.synchronize()
+    g = {k: getattr(res, k).cpu().numpy() for k in ("tokens", "accepted", "p_draft", "status")}
+    zh, dh = z.float().cpu().numpy(), d.float().cpu().numpy()
+    xh, Lh = x.cpu().numpy(), L.cpu().numpy()
+    rows = sorted({0, B - 1, *np.random.default_rng(7).integers(0, B, 8).tolist()})
+    gs = {k: v[rows] for k, v in g.items()}
+    parts = [S.spec_accept_sampled(zh[b:b + 1], dh[b:b + 1], xh[b:b + 1], Lh[b:b + 1], 0.8, 0.8, 0.95, 0.05, 77, 0,
+                                   row_base=b) for b in rows]
+    o = {k: np.concatenate([p_[k] for p_ in parts]) for k in parts[0]}
+    print(compare(gs, o, "bench size", max_near=0.5))
+
+
 def test_flat_distribution_deep_top_p_cut():
     # small logit spread: the top-p cut falls deep in the vocabulary, in a
     # crossing bin with many entries.  Distinct logits then sit ~3e-5 of mass
