@@ -272,16 +272,22 @@ __device__ __forceinline__ void row_rounds(const T* row, int64_t V, F&& f) {
     if constexpr (VEC) {
         constexpr int W = VecRound<T>::W;
         const int64_t nv = V / W;
-        const uint4* p = reinterpret_cast<const uint4*>(row);
+        // buffer loads: a 32-bit offset per lane, the round's step in the
+        // scalar offset, and reads past the row's end return zeros
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, (int)(nv * 16), 0x00020000);
         constexpr int64_t kStep = (int64_t)kTS * kU;
-        // the next round's loads go out before this round is consumed
-        // (clamped addresses: past the row they read its last vector again)
+        auto ld16 = [&](int64_t v) -> uint4 {
+            const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(t * 16), (int)(v * 16), 0);
+            return make_uint4(r.x, r.y, r.z, r.w);
+        };
         VecRound<T> z, nz;
 #pragma unroll
-        for (int u = 0; u < kU; ++u) z.r[u] = p[min((int64_t)u * kTS + t, nv - 1)];
+        for (int u = 0; u < kU; ++u) z.r[u] = ld16((int64_t)u * kTS);
         for (int64_t v0 = 0; v0 < nv; v0 += kStep) {
 #pragma unroll
-            for (int u = 0; u < kU; ++u) nz.r[u] = p[min(v0 + kStep + (int64_t)u * kTS + t, nv - 1)];
+            for (int u = 0; u < kU; ++u) nz.r[u] = ld16(v0 + kStep + (int64_t)u * kTS);
             uint32_t ok = 0u;
 #pragma unroll
             for (int u = 0; u < kU; ++u)
