@@ -130,6 +130,31 @@ def test_bench_size_sampled_rows():
     print(compare(gs, o, "bench size", max_near=0.5))
 
 
+@pytest.mark.parametrize("bf16", [False, True])
+def test_top_p_alone_peaked(bf16):
+    # top-p alone on peaked distributions (a few dozen dominant tokens per
+    # position), the shape of real next-token distributions
+    rng = np.random.default_rng(23 + bf16)
+    B, K, V, T, tp = 8, 3, 50000, 0.9, 0.8
+    z = rng.normal(0, 2.0, (B, K + 1, V))
+    for b in range(B):
+        for i in range(K + 1):
+            z[b, i, rng.choice(V, 30, replace=False)] += rng.uniform(8.0, 12.0, 30)
+    z = z.astype(np.float32)
+    d = (z[:, :K] + rng.normal(0, 0.7, (B, K, V))).astype(np.float32)
+    if bf16:
+        z = torch.from_numpy(z).to(torch.bfloat16).float().numpy()
+        d = torch.from_numpy(d).to(torch.bfloat16).float().numpy()
+    x = np.zeros((B, K), np.int32)
+    for b in range(B):
+        for i in range(K):
+            q = S.filtered(d[b, i], T, float(np.float32(tp)), 0.0)[0]
+            x[b, i] = rng.choice(V, p=q / q.sum())
+    g, o = run(z, d, x, rng.integers(0, K + 1, B).astype(np.int32), T=T, top_p=tp, min_p=0.0, seed=8, offset=2,
+               bf16=bf16, label="top-p alone, peaked")
+    print(compare(g, o, ("top-p alone", bf16), max_near=0.5))
+
+
 def test_flat_distribution_deep_top_p_cut():
     # small logit spread: the top-p cut falls deep in the vocabulary, in a
     # crossing bin with many entries.  Distinct logits then sit ~3e-5 of mass
@@ -159,7 +184,8 @@ def test_different_draft_temperature_and_edges():
 
 
 def _single_pass_rows(V, K, rng):
-    """Rows that stress the one-pass statistics with min-p on: a rising ramp
+    """Rows that stress the statistics pass in every filter mode (the one
+    pass of min-p, the general passes without it): a rising ramp
     (the reference max grows every round), a jump of 600 mid-row (the round
     is summed again against the new reference), a -inf prefix (no finite
     reference for several rounds), a row that is -inf but for its last
@@ -184,9 +210,9 @@ def _single_pass_rows(V, K, rng):
 
 
 @pytest.mark.parametrize("bf16", [False, True])
-@pytest.mark.parametrize("top_p", [1.0, 0.9])
-def test_min_p_one_pass_edges(bf16, top_p):
-    V, K, T, mp = 20000 + (3 if not bf16 else 0), 2, 0.8, 0.05
+@pytest.mark.parametrize("top_p,mp", [(1.0, 0.05), (0.9, 0.05), (0.9, 0.0), (1.0, 0.0)])
+def test_one_pass_edges(bf16, top_p, mp):
+    V, K, T = 20000 + (3 if not bf16 else 0), 2, 0.8
     rng = np.random.default_rng(41 + bf16)
     z, d = _single_pass_rows(V, K, rng)
     if bf16:
@@ -208,11 +234,11 @@ def test_min_p_one_pass_edges(bf16, top_p):
             if q is not None:
                 x[b, i] = rng.choice(V, p=q / q.sum())
     g, o = run(z, d, x, np.full(B, K, np.int32), T=T, top_p=top_p, min_p=mp, seed=5, offset=1, bf16=bf16,
-               label=f"one-pass edges top_p={top_p}")
+               label=f"one-pass edges top_p={top_p} min_p={mp}")
     assert o["status"][5] == S.ROW_NONFINITE and o["status"][6] == S.ROW_NONFINITE
     assert (g["status"][5] & S.ROW_NONFINITE) and (g["status"][6] & S.ROW_NONFINITE)
     assert not np.any(o["status"][[0, 1, 2, 3, 4, 7]])
-    compare(g, o, ("one-pass edges", bf16, top_p), max_near=0.5)
+    compare(g, o, ("one-pass edges", bf16, top_p, mp), max_near=0.5)
 
 
 def test_status_bits():
