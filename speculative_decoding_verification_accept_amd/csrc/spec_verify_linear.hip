@@ -638,6 +638,23 @@ __device__ __forceinline__ void dma_prologue(const DmaAddr<Cfg>& A, int wave, in
     ((st0 + Ds < st1 ? dma_issue<Cfg, Ds>(A, wave, st0 + Ds) : void()), ...);
 }
 
+// Workgroups are dealt to the XCDs in turn (workgroup id mod kXcds), and
+// each XCD has an L2 of its own.  This remap of the (m-tile, n-tile) grid
+// gives XCD x a contiguous run of tiles in m-fastest order, so the m-tiles
+// that share a column strip of W (and read it at about the same time) run on
+// one XCD and fetch it through one L2.  It is a bijection of the grid
+// whatever the XCD count, which only decides how well it places tiles.
+constexpr int kXcds = 8;
+__device__ __forceinline__ void xcd_tile(int64_t& mt, int64_t& nt) {
+    const int64_t MT = gridDim.x, T = MT * gridDim.y;
+    const int64_t g = mt + MT * nt;  // dispatch order within a split
+    const int64_t x = g % kXcds, j = g / kXcds;
+    const int64_t per = T / kXcds, rem = T % kXcds;
+    const int64_t t = x < rem ? x * (per + 1) + j : rem * (per + 1) + (x - rem) * per + j;
+    mt = t % MT;
+    nt = t / MT;
+}
+
 template <typename Cfg>
 __global__ __launch_bounds__(Cfg::NT) void k_dma(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                                                  void* __restrict__ Y, int y_bf16, int64_t M, int64_t N,
@@ -648,8 +665,10 @@ __global__ __launch_bounds__(Cfg::NT) void k_dma(const uint16_t* __restrict__ X,
     // wave-uniform, so the loads' LDS base (M0) and their branches stay scalar
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int wm = wave / Cfg::NWN, wn = wave % Cfg::NWN;
-    const int64_t m0 = (int64_t)blockIdx.x * Cfg::BM;
-    const int64_t n0 = ((int64_t)blockIdx.y + ntile0) * Cfg::BN;
+    int64_t mt = blockIdx.x, nt = blockIdx.y;
+    if (gridDim.x > 1) xcd_tile(mt, nt);
+    const int64_t m0 = mt * Cfg::BM;
+    const int64_t n0 = (nt + ntile0) * Cfg::BN;
     const int split = blockIdx.z;
     const int64_t nst = (K + Cfg::BK - 1) / Cfg::BK;
     const int64_t st0 = split * nst / splits, st1 = (split + 1) * nst / splits;
@@ -758,8 +777,8 @@ using TileL = TileCfg<192, 256, 64, 96, 64>;
 using TileB = TileCfg<256, 128, 64, 64, 64>;
 using DmaS = DmaCfg<128, 128, 64, 2, 4, 4>;   // M in (16, 128], or (128, 256] on narrow N
 using DmaL = DmaCfg<192, 256, 32, 2, 4, 5>;   // M in (128, 192] on a wide N (lm-head)
-using DmaB = DmaCfg<256, 128, 32, 4, 2, 5>;   // M in (256, 768]
-using DmaH = DmaCfg<256, 256, 32, 2, 4, 4>;   // M > 768
+using DmaB = DmaCfg<256, 128, 32, 4, 2, 5>;   // M in (256, 512]
+using DmaH = DmaCfg<256, 256, 32, 2, 4, 4>;   // M > 512
 
 enum Kern { kStrip1, kStrip2, kTileS, kTileL, kTileB, kDmaS, kDmaL, kDmaB, kDmaH };
 
@@ -800,7 +819,10 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
     } else if (K % 64 == 0 && M <= 256) {
         pick(kDmaS, DmaS::BM, DmaS::BN, DmaS::BK);
     } else if (K % 32 == 0 && M > 256) {
-        if (M <= 768) pick(kDmaB, DmaB::BM, DmaB::BN, DmaB::BK);
+        // past 512 rows the 256 x 256 tile: at M = 768, N = 14336 its 168
+        // tiles fit one round on 256 compute units where the 336 tiles of
+        // 256 x 128 need two (measured 111 us against 152 us)
+        if (M <= 512) pick(kDmaB, DmaB::BM, DmaB::BN, DmaB::BK);
         else pick(kDmaH, DmaH::BM, DmaH::BN, DmaH::BK);
     } else if (M > 128 && M <= 192 && (N + TileL::BN - 1) / TileL::BN >= cus) {
         pick(kTileL, TileL::BM, TileL::BN, TileL::BK);

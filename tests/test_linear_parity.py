@@ -41,6 +41,10 @@ def _check(Y, ref, label):
 @pytest.mark.parametrize("M,N,K", [
     (1, 128, 32), (5, 136, 40), (16, 256, 64), (17, 264, 200), (33, 1024, 256),
     (64, 384, 512), (65, 520, 1000), (130, 1032, 96), (300, 256, 520), (257, 8, 8),
+    # several m-tiles through the tile remap: a grid of fewer tiles than
+    # XCDs (without and with split-K), and a ragged 15-tile grid, on the
+    # 128 x 128, 256 x 128 and 256 x 256 tiles
+    (200, 136, 128), (300, 264, 512), (600, 392, 256), (520, 1160, 320),
 ])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_small_shapes_every_element(M, N, K, out_dtype):
@@ -76,6 +80,13 @@ def test_sweep_shapes_sampled(M):
     print(f"[spec_verify_linear] sweep M={M} N={workloads.FFN_N} K={workloads.HIDDEN}", flush=True)
     r = _sampled(M, workloads.FFN_N, workloads.HIDDEN, torch.bfloat16, seed=1000 + M)
     print(f"M={M} worst scaled err {r:.3g}")
+
+
+def test_between_sweep_sizes_sampled():
+    # M = 768 takes the 256 x 256 tile in one round of 168 tiles
+    print(f"[spec_verify_linear] M=768 N={workloads.FFN_N} K={workloads.HIDDEN}", flush=True)
+    r = _sampled(768, workloads.FFN_N, workloads.HIDDEN, torch.bfloat16, seed=1768)
+    print(f"M=768 worst scaled err {r:.3g}")
 
 
 def test_lmhead_sampled():
