@@ -45,6 +45,8 @@ def _check(Y, ref, label):
     # XCDs (without and with split-K), and a ragged 15-tile grid, on the
     # 128 x 128, 256 x 128 and 256 x 256 tiles
     (200, 136, 128), (300, 264, 512), (600, 392, 256), (520, 1160, 320),
+    # past 512 rows with K a multiple of 32 but not of 64: the 256 x 128 tile
+    (600, 392, 288),
 ])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_small_shapes_every_element(M, N, K, out_dtype):
