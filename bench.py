@@ -59,6 +59,20 @@ def _events(torch, n):
     return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
+def _single_call_us(torch, fn, n=21):
+    """Latency of one call: events around it and a synchronisation after
+    each, so that no call overlaps another; the median over n calls."""
+    ts = []
+    for i in range(n):
+        e0, e1 = _events(torch, 2)
+        e0.record()
+        fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    return sorted(ts)[n // 2]
+
+
 def bench_step(torch, sv, workloads, steps, warmup):
     dev = torch.device("cuda:0")
     B, K, V, H = 32, 5, workloads.LMHEAD_N, workloads.HIDDEN
@@ -104,11 +118,14 @@ def bench_step(torch, sv, workloads, steps, warmup):
         step(warmup + steps + i, evs[i])
     torch.cuda.synchronize()
     gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    # pass 3: one step at a time, the GPU idle before each
+    latency_ms = _single_call_us(torch, lambda i: step(warmup + 2 * steps + i)) * 1e-3
     acc = out.accepted.cpu()
     emitted = float((acc + 1).float().mean())
     gemm_bytes = 2 * H * V + 2 * M * H + 4 * M * V
     gemm_flops = 2 * M * H * V
-    return dict(ms_per_step=ms_per_step, positions=M, gemm_ms=gemm_ms, gemm_bytes=gemm_bytes,
+    return dict(ms_per_step=ms_per_step, latency_ms=latency_ms, positions=M, gemm_ms=gemm_ms,
+                gemm_bytes=gemm_bytes,
                 gemm_flops=gemm_flops, mean_emitted=emitted,
                 state=dict(hidden=hidden, W=W, logits=logits, q=q, x=x, L=L, B=B, K=K, V=V))
 
@@ -147,10 +164,16 @@ def bench_accept_large(torch, sv, workloads, reps=60, nsets=5):
     t1.record()
     torch.cuda.synchronize()
     us = t0.elapsed_time(t1) * 1e3 / (reps * nsets)
+
+    def one(i):
+        z, q, x, L = sets[i % nsets]
+        sv.accept(z, q, x, L, temperature=0.8, seed=77, offset=i % nsets, workspace=ws,
+                  out=outs[i % nsets])
+    lat = _single_call_us(torch, one)
     pos = sum(positions) / nsets
     b = sum(byts) / nsets
     return dict(workload="spec_accept B=64 K=7 V=128256 bf16 T=0.8 ragged L~U{1..7}, 5 rotating sets",
-                us_per_call=us, positions_per_call=pos, positions_per_s=pos / us * 1e6,
+                us_per_call=us, latency_us=lat, positions_per_call=pos, positions_per_s=pos / us * 1e6,
                 algorithmic_bytes=b, achieved_GBs=b / us * 1e-3,
                 frac_hbm=b / us * 1e-3 / HBM_PEAK_GBS)
 
@@ -182,6 +205,11 @@ def bench_accept_sampled(torch, sv, workloads, reps=30, nsets=4):
     t1.record()
     torch.cuda.synchronize()
     us = t0.elapsed_time(t1) * 1e3 / reps
+
+    def one(i):
+        z, d, x, L = sets[i % nsets]
+        sv.accept_sampled(z, d, x, L, offset=i, **kw)
+    lat = _single_call_us(torch, one)
     nrows = sum(rows) / nsets
     # every target row 0..L_b and draft row 0..L_b-1 read once, plus the
     # token gathers and outputs
@@ -190,7 +218,7 @@ def bench_accept_sampled(torch, sv, workloads, reps=30, nsets=4):
     return dict(workload="spec_accept_sampled B=64 K=7 V=128256 bf16 target and draft logits, "
                          "T=0.8, top-p 0.95, min-p 0.05, ragged L~U{1..7}, draft = its top logit, "
                          f"{nsets} rotating sets",
-                us_per_call=round(us, 2), distributions_per_call=nrows,
+                us_per_call=round(us, 2), latency_us=round(lat, 2), distributions_per_call=nrows,
                 positions_per_s=round((nrows + B) / 2 / us * 1e6, 1),
                 algorithmic_bytes=byts, achieved_GBs=round(gbs, 1),
                 frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
@@ -511,6 +539,7 @@ def main():
                      "algorithmic_bytes": r["gemm_bytes"],
                      "tflops": round(r["gemm_flops"] / (r["gemm_ms"] * 1e-3) * 1e-12, 1)},
         "mean_emitted_per_row": round(r["mean_emitted"], 3),
+        "single_step_latency_ms": round(r["latency_ms"], 4),
     }
     if not args.no_breakdown:
         acc = bench_accept_large(torch, sv, workloads)
