@@ -73,6 +73,42 @@ def _single_call_us(torch, fn, n=21):
     return sorted(ts)[n // 2]
 
 
+def measured_peaks(torch, reps=10):
+    """Practical peaks of this GPU, measured in the same process, as context
+    beside the fractions of the published peaks: a device-to-device copy of
+    1 GiB (bytes read plus bytes written per second) and the vendor library's
+    bf16 product of two 8192 x 8192 matrices."""
+    dev = torch.device("cuda:0")
+    a = torch.ones(1 << 29, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0, t1 = _events(torch, 2)
+    t0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    t1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * a.numel() * 2 * reps / (t0.elapsed_time(t1) * 1e-3) * 1e-9
+    del a, b
+    n = 8192
+    X = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    W = torch.randn(n, n, device=dev).to(torch.bfloat16)
+    Y = torch.matmul(X, W)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(reps):
+        torch.matmul(X, W, out=Y)
+    t1.record()
+    torch.cuda.synchronize()
+    tflops = 2 * n ** 3 * reps / (t0.elapsed_time(t1) * 1e-3) * 1e-12
+    del X, W, Y
+    return {"copy_GBs": round(copy_gbs, 1), "copy_frac_of_peak": round(copy_gbs / HBM_PEAK_GBS, 4),
+            "matmul_bf16_TFLOPs": round(tflops, 1),
+            "matmul_frac_of_peak": round(tflops / BF16_PEAK_TFLOPS, 4),
+            "how": "1 GiB device-to-device copy (read + written bytes); torch.matmul bf16 8192^3"}
+
+
 def bench_step(torch, sv, workloads, steps, warmup):
     dev = torch.device("cuda:0")
     B, K, V, H = 32, 5, workloads.LMHEAD_N, workloads.HIDDEN
@@ -541,6 +577,9 @@ def main():
         "mean_emitted_per_row": round(r["mean_emitted"], 3),
         "single_step_latency_ms": round(r["latency_ms"], 4),
     }
+    peaks = measured_peaks(torch)
+    line["measured_peaks"] = peaks
+    line["roofline"]["frac_of_measured_copy"] = round(gemm_gbs / peaks["copy_GBs"], 4)
     if not args.no_breakdown:
         acc = bench_accept_large(torch, sv, workloads)
         acc = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in acc.items()}
