@@ -557,8 +557,10 @@ struct DmaAddr {
 // as inline assembly: the compiler neither tracks these loads nor inserts
 // waits for them, so every wait on them is explicit (wait_vm_lgkm).
 __device__ __forceinline__ void lds_dma16(const char* src, uint32_t lds_base) {
-    // M0 holds the LDS base of the load; no code of this file keeps a value in
-    // M0 across this statement.
+    // M0 holds the LDS base of the load.  Sound only while the compiler keeps
+    // no value of its own in M0 in these kernels: in the gfx950 assembly every
+    // M0 access of a k_dma instantiation is one of these writes, one per load
+    // (checked on every build of the test suite, tests/test_isa_m0.py).
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
 }
 template <typename Cfg, int D>
