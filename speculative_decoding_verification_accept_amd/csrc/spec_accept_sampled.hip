@@ -72,7 +72,8 @@ constexpr int kW = kT / kWave;
 constexpr int kChunkBytes = 16384;
 constexpr int kBins = 512;                  // coarse bins of u, 1/16 wide
 constexpr float kBinScale = 16.f;
-constexpr int kCand = 4096;                 // crossing-bin entries resolved exactly
+constexpr int kCand = 4096;                 // entries resolved exactly: the min-p candidates of the
+                                            // one-pass reader, or the top-p crossing bin
 constexpr int kMaxChunks = 1024;
 constexpr int kRowStride = 64;              // ints per row record (256 bytes)
 constexpr int kCnt = 0;                     // phase-2 arrivals
