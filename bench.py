@@ -41,6 +41,8 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_SUMMARY = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                "traffic_lmhead_gemm_and_accept.md")
 BF16_PEAK_TFLOPS = 2500.0
+WARMUP_S = 0.5      # at least this long of untimed steps before the timed window
+TEL_STEPS = 64      # untimed steps whose accept passes feed the acceptance telemetry
 
 
 def _parse():
@@ -136,34 +138,77 @@ def bench_step(torch, sv, workloads, steps, warmup):
         if ev is not None:
             ev[1].record()
         sv.accept(z3, q, x, L, temperature=0.6, seed=seed, offset=i, workspace=ws_acc, out=out)
+        if ev is not None:
+            ev[2].record()
 
-    for i in range(warmup):
-        step(i)
+    # warm-up: the requested steps, then more until WARMUP_S seconds of
+    # steps have run, so that the timed window starts at steady clocks
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < warmup or time.perf_counter() - t_w < WARMUP_S:
+        step(n_warm)
+        n_warm += 1
+        if n_warm % 50 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
+    base = n_warm
     # pass 1: whole-step throughput, nothing between launches
     t0, t1 = _events(torch, 2)
     t0.record()
     for i in range(steps):
-        step(warmup + i)
+        step(base + i)
     t1.record()
     torch.cuda.synchronize()
     ms_per_step = t0.elapsed_time(t1) / steps
-    # pass 2: the dominant kernel's own duration (events around each launch)
-    evs = [_events(torch, 2) for _ in range(steps)]
+    # pass 2: per-step events (the dominant kernel's call, and the whole step)
+    evs = [_events(torch, 3) for _ in range(steps)]
     for i in range(steps):
-        step(warmup + steps + i, evs[i])
+        step(base + steps + i, evs[i])
     torch.cuda.synchronize()
     gemm_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / steps
+    step_ms = sorted(e[0].elapsed_time(e[2]) for e in evs)
+    step_median_ms = step_ms[steps // 2]
     # pass 3: one step at a time, the GPU idle before each
-    latency_ms = _single_call_us(torch, lambda i: step(warmup + 2 * steps + i)) * 1e-3
+    latency_ms = _single_call_us(torch, lambda i: step(base + 2 * steps + i)) * 1e-3
+    # pass 4 (untimed): acceptance telemetry over TEL_STEPS further steps,
+    # spec_adapt fed with each step's accepted lengths
+    tel = sv.adapt_telemetry(dev)
+    st_ad = sv.adapt_state(B, dev)
+    nxt = torch.empty(B, dtype=torch.int32, device=dev)
+    resid_zero = torch.zeros((), dtype=torch.int64, device=dev)
+    for i in range(TEL_STEPS):
+        step(base + 3 * steps + 64 + i)
+        sv.adapt(out.accepted, L, st_ad, tel, K=K, k_min=1, k_max=K, out=nxt)
+        resid_zero += ((out.status & sv.ROW_RESID_ZERO) != 0).sum()
+    torch.cuda.synchronize()
     acc = out.accepted.cpu()
     emitted = float((acc + 1).float().mean())
     gemm_bytes = 2 * H * V + 2 * M * H + 4 * M * V
     gemm_flops = 2 * M * H * V
-    return dict(ms_per_step=ms_per_step, latency_ms=latency_ms, positions=M, gemm_ms=gemm_ms,
-                gemm_bytes=gemm_bytes,
+    return dict(ms_per_step=ms_per_step, step_median_ms=step_median_ms, latency_ms=latency_ms,
+                warmup_steps_run=n_warm, positions=M, gemm_ms=gemm_ms, gemm_bytes=gemm_bytes,
                 gemm_flops=gemm_flops, mean_emitted=emitted,
+                telemetry=_telemetry(sv, tel, K, int(resid_zero)),
                 state=dict(hidden=hidden, W=W, logits=logits, q=q, x=x, L=L, B=B, K=K, V=V))
+
+
+def _telemetry(sv, tel, K, resid_zero_rows):
+    """Acceptance telemetry of the step's accept passes, from spec_adapt's
+    counters: the acceptance rate, mean accepted length, per-position
+    acceptance and the (draft length, accepted) histogram."""
+    c = sv.telemetry_counters(tel)
+    tested, accepted = c["tested_at"][:K], c["accepted_at"][:K]
+    hist = c["hist"]
+    al = {str(a): int(hist[:, a].sum()) for a in range(K + 1) if hist[:, a].sum()}
+    return {"steps": int(c["calls"]), "rows": c["rows"], "invalid_rows": c["invalid_rows"],
+            "acceptance_rate": round(c["accepted"] / max(c["tested"], 1), 4),
+            "mean_accepted_drafts": round(c["accepted"] / max(c["rows"], 1), 4),
+            "mean_emitted_per_pass": round(c["emitted"] / max(c["rows"], 1), 4),
+            "per_position_acceptance": [round(int(a) / int(t), 4) if t else None
+                                        for a, t in zip(accepted, tested)],
+            "accepted_drafts_histogram": al,
+            "zero_residual_rows": resid_zero_rows,
+            "source": "spec_adapt counters over the accept passes of the telemetry steps"}
 
 
 def bench_accept_large(torch, sv, workloads, reps=60, nsets=5):
@@ -400,6 +445,20 @@ def bench_control(torch, sv, sweep, reps=200):
     return out
 
 
+def _host():
+    """The host CPU model and its logical core count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "logical_cpus": os.cpu_count()}
+
+
 def _timed(fn, budget_s):
     """Runs fn repeatedly for about budget_s (at least once): seconds per run."""
     n, t0 = 0, time.perf_counter()
@@ -488,14 +547,15 @@ def cpu_baseline(torch, workloads, st, budget_s=12.0):
     q = st["q"].cpu().numpy()
     x = st["x"].cpu().numpy()
     L = st["L"].cpu().numpy()
-    t_gemm, t_acc, n = 0.0, 0.0, 0
+    t_gemm, t_acc, n, near_rows = 0.0, 0.0, 0, 0
     t_start = time.perf_counter()
     while n == 0 or time.perf_counter() - t_start < budget_s:
         t0 = time.perf_counter()
         oracle.verify_linear(Xh, Wh)
         t1 = time.perf_counter()
-        oracle.spec_accept(z, q, x, L, 0.6, 0x5EED, n, nthreads=cores)
+        o = oracle.spec_accept(z, q, x, L, 0.6, 0x5EED, n, nthreads=cores)
         t2 = time.perf_counter()
+        near_rows += int(np.sum((o["near_acc"] >= 0) | (o["near_smp"] > 0)))
         t_gemm += (t1 - t0) * (V / ncols)
         t_acc += t2 - t1
         n += 1
@@ -503,6 +563,10 @@ def cpu_baseline(torch, workloads, st, budget_s=12.0):
     rows = _cpu_rows(workloads, cores)
     return dict(value=round(B * (K + 1) / per_step, 2), unit="verified positions/s", paths=rows,
                 cores=max(cores, blas_threads), kind="oracle",
+                near_threshold_rows={"rows": near_rows, "of": n * B,
+                                     "what": "rows of the oracle's runs on the step's logits whose "
+                                             "acceptance test or draw lies within 1e-6 of its "
+                                             "threshold"},
                 sample=(f"{n} step(s): fp64 numpy GEMM on {ncols} of {V} lm-head columns scaled "
                         f"x{V / ncols:.0f} ({t_gemm / n:.2f} s/step) + fp64 C accept oracle on all "
                         f"{B} rows ({t_acc / n:.2f} s/step, {cores} OpenMP threads)"))
@@ -543,7 +607,7 @@ def main():
         print(json.dumps(bench_control(torch, sv, [])))
         return
 
-    from speculative_decoding_verification_accept_amd import traffic
+    import traffic
     counted = traffic.read_committed(TRAFFIC_SUMMARY)   # None once the kernels changed
 
     r = bench_step(torch, sv, workloads, args.steps, args.warmup)
@@ -575,7 +639,14 @@ def main():
                      "algorithmic_bytes": r["gemm_bytes"],
                      "tflops": round(r["gemm_flops"] / (r["gemm_ms"] * 1e-3) * 1e-12, 1)},
         "mean_emitted_per_row": round(r["mean_emitted"], 3),
+        "ms_per_step_median": round(r["step_median_ms"], 5),
         "single_step_latency_ms": round(r["latency_ms"], 4),
+        "warmup_steps_run": r["warmup_steps_run"],
+        "timing": (f"window: events around {args.steps} back-to-back steps after at least "
+                   f"{args.warmup} steps and {WARMUP_S} s of untimed warm-up; median: per-step "
+                   "events in a second pass; latency: one step with the GPU idle, median of 21"),
+        "acceptance_telemetry": r["telemetry"],
+        "host": _host(),
     }
     peaks = measured_peaks(torch)
     line["measured_peaks"] = peaks
@@ -592,6 +663,7 @@ def main():
                              "control": bench_control(torch, sv, sweep["sweep"])}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, workloads, r["state"])
+        line["acceptance_telemetry"]["near_threshold_rows"] = line["cpu_baseline"]["near_threshold_rows"]
     print(json.dumps(line), flush=True)
 
 

@@ -33,6 +33,7 @@
 #include "spec_verify.h"
 #include "device_common.hpp"
 
+#include <atomic>
 #include <utility>
 
 namespace specv {
@@ -240,14 +241,17 @@ struct TileRegs {
 };
 
 // Loop-invariant per-thread addressing of k_tile.  Global loads are buffer
-// loads: the per-lane byte offset is fixed for the whole K loop and a stage
-// only moves the scalar offset; a lane whose element lies outside the matrix
-// gets an offset past the buffer's end, which the hardware reads as zero.
+// loads whose whole byte offset is the per-lane offset: the hardware's range
+// check covers that offset and not the scalar one, so an element outside the
+// matrix (a column past N, a row past M, a k past K) gets the offset kOOB,
+// past the buffer's end, and reads as zero.  The host routes a matrix of
+// 2 GiB or more elsewhere, so every in-range offset is below kOOB.
 template <typename Cfg>
 struct TileAddr {
     __amdgpu_buffer_rsrc_t wr, xr;
-    uint32_t wv[Cfg::WBLK];   // W block (8 rows) byte offset within a stage, row 0
-    uint32_t xv[Cfg::XV];     // X vector byte offset within a stage
+    uint32_t wv[Cfg::WBLK];   // W block (8 rows) byte offset at stage 0, row 0 (kOOB past N)
+    uint32_t wk[Cfg::WBLK];   // k of the block's row 0 within a stage
+    uint32_t xv[Cfg::XV];     // X vector byte offset at stage 0 (kOOB past M)
     uint32_t wlds[Cfg::WBLK]; // LDS byte offset of the block's column 0 (within the W tile)
     uint32_t xlds[Cfg::XV];   // LDS byte offset of the X vector (within the X tile)
     uint32_t row_bytes;       // N * 2
@@ -270,6 +274,7 @@ __device__ __forceinline__ void tile_addr(const uint16_t* X, const uint16_t* W, 
         const int kb = q / (Cfg::BN / 8), nb = q % (Cfg::BN / 8);
         const int64_t n = n0 + 8 * nb;
         A.wv[j] = (q < Cfg::WBLK_TOTAL && n < N) ? (uint32_t)(((int64_t)8 * kb * N + n) * 2) : kOOB;
+        A.wk[j] = (uint32_t)(8 * kb);
         // rows 8 nb .. 8 nb + 7 of the transposed tile share the swizzle (n >> 4) = nb >> 1
         A.wlds[j] = (uint32_t)((8 * nb) * Cfg::LDK * 2 + 16 * w_group(kb, nb >> 1));
     }
@@ -288,22 +293,25 @@ __device__ __forceinline__ uint4 bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, 
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
 
-// Global loads of the stage starting at k0.  W rows past K lie past the end
-// of W (zero); X vectors past K within a row are masked only when the stage
-// crosses K.
+// Global loads of the stage starting at k0.  W rows and X vectors past K
+// (only when the stage crosses K, K being a multiple of 8) get the offset
+// kOOB and read as zero; no scalar offset is used.
 template <typename Cfg>
 __device__ __forceinline__ void tile_load(const TileAddr<Cfg>& A, int64_t K, int64_t k0,
                                           TileRegs<Cfg>& R) {
     const uint32_t wst = (uint32_t)(k0 * A.row_bytes);
-#pragma unroll
-    for (int j = 0; j < Cfg::WBLK; ++j)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) R.w[j][r] = bload(A.wr, A.wv[j], wst + r * A.row_bytes);
     const bool tail = k0 + Cfg::BK > K;
 #pragma unroll
+    for (int j = 0; j < Cfg::WBLK; ++j) {
+        // a block's 8 rows are all below K or all at or past it
+        const bool wout = A.wv[j] == kOOB || (tail && k0 + A.wk[j] >= K);
+#pragma unroll
+        for (int r = 0; r < 8; ++r) R.w[j][r] = bload(A.wr, wout ? kOOB : A.wv[j] + wst + r * A.row_bytes, 0u);
+    }
+#pragma unroll
     for (int j = 0; j < Cfg::XV; ++j) {
-        const uint32_t vo = (tail && k0 + A.x_kok[j] >= K) ? kOOB : A.xv[j];
-        R.x[j] = bload(A.xr, vo, (uint32_t)(k0 * 2));
+        const bool xout = A.xv[j] == kOOB || (tail && k0 + A.x_kok[j] >= K);
+        R.x[j] = bload(A.xr, xout ? kOOB : A.xv[j] + (uint32_t)(k0 * 2), 0u);
     }
 }
 
@@ -803,7 +811,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
     // the strip kernel for a few rows; from 17 rows the 128x128 tile (K a
     // multiple of 64) measured faster on MI355X (31.4 vs 34.0 us at M = 32,
     // N = 14336, K = 4096)
-    if (M <= 16 || (M <= 32 && K % 64 != 0)) {
+    auto strip_plan = [&]() {
         p.kern = M <= 16 ? kStrip1 : kStrip2;
         const int mt = M <= 16 ? 1 : 2;
         p.mtiles = (M + 16 * mt - 1) / (16 * mt);
@@ -811,7 +819,8 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
         p.nl = 1;
         p.l[0] = Launch{0, p.ntiles, 1};
         return p;
-    }
+    };
+    if (M <= 16 || (M <= 32 && K % 64 != 0)) return strip_plan();
     int BM, BN, BK;
     auto pick = [&](Kern k, int bm, int bn, int bk) { p.kern = k; BM = bm; BN = bn; BK = bk; };
     if (K % 64 == 0 && M <= 128) {
@@ -834,6 +843,11 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
     } else {
         pick(kTileB, TileB::BM, TileB::BN, TileB::BK);
     }
+    // k_tile addresses its operands with 32-bit buffer offsets below kOOB:
+    // a shape that would give it an operand of 2 GiB or more takes the strip
+    // kernel (flat loads) instead, whatever M is
+    const bool tile = p.kern == kTileS || p.kern == kTileL || p.kern == kTileB;
+    if (tile && ((uint64_t)K * N * 2 >= kOOB || (uint64_t)M * K * 2 >= kOOB)) return strip_plan();
     p.BN = BN;
     p.mtiles = (M + BM - 1) / BM;
     p.ntiles = (N + BN - 1) / BN;
@@ -860,11 +874,23 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
     return p;
 }
 
+// Compute units of the current device, queried once per device and cached
+// (the plan depends on it; a query per call would cost a runtime round trip).
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
 int device_cus() {
-    int dev = 0, cus = 0;
+    int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = g_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 256;
-    return cus > 0 ? cus : 256;
+    cus = cus > 0 ? cus : 256;
+    if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(cus, std::memory_order_relaxed);
+    return cus;
 }
 
 // NP: row stride of the partials, covering columns l.t0 BN .. l.t0 BN + NP - 1.

@@ -3,7 +3,7 @@ totals, and the digest gate that keeps stale figures out of the bench line."""
 import csv
 import os
 
-from speculative_decoding_verification_accept_amd import traffic
+import traffic
 
 
 def _csv(path, rows):

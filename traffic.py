@@ -2,7 +2,7 @@
 
 Run under a counter profiler, for example
 
-    rocprofv3 --pmc FETCH_SIZE -- python3 -m speculative_decoding_verification_accept_amd.traffic
+    rocprofv3 --pmc FETCH_SIZE -- python3 traffic.py
 
 It launches, on synthetic inputs already resident on the GPU:
   * a plain device-to-device copy of 256 MiB (``copy``), the calibration of
@@ -25,7 +25,8 @@ import re
 import sys
 
 COPY_BYTES = 256 << 20
-PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PKG = os.path.join(ROOT, "speculative_decoding_verification_accept_amd")
 
 
 def source_digest() -> str:
@@ -180,5 +181,5 @@ def main(argv=None):
 
 
 if __name__ == "__main__":
-    sys.path.insert(0, os.path.dirname(PKG))
+    sys.path.insert(0, ROOT)
     main()
