@@ -62,12 +62,10 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 #define SPEC_ROW_ZERO_Q 8      /* q_i(x_i) not > 0 at a position < L_b (stochastic mode) */
 #define SPEC_ROW_RESID_ZERO 16 /* informational: the residual max(p - q, 0) summed to 0,
                                   the token was drawn from p instead */
-#define SPEC_ROW_FILTER_COARSE 64 /* informational (spec_accept_sampled): a top-p cut fell in
-                                  a bin of more than 4096 entries, which was kept whole */
-#define SPEC_ROW_STALLED 32    /* the row's workgroups did not all make progress within the
-                                  wait bound (about 0.1 s); out_accepted[b] = -1, the rest
-                                  of the row's outputs are unspecified, and the workspace
-                                  must be zero-filled again before its next use */
+#define SPEC_ROW_STALLED 32    /* a workgroup of the row waited for the row's decision past
+                                  the wait bound (about 0.1 s) and gave up; out_accepted[b]
+                                  = -1 and out_tokens[b] is all -1 (out_p_draft[b] is
+                                  unspecified).  The workspace stays valid for later calls */
 
 /* Limits. */
 #define SPEC_MAX_DRAFT 255 /* K <= 255 */
@@ -123,10 +121,11 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
  *                  bytes, 16-byte aligned.  Its first 256 * B bytes hold
  *                  per-row counters through which the workgroups of a row
  *                  hand work to one another: they must be ZERO when the call
- *                  starts, and every call leaves them zero again.  So a
- *                  workspace zero-filled once serves every later call with
- *                  the same or fewer rows (any K, V).  Calls that may run
- *                  concurrently need separate workspaces.
+ *                  starts, and every call leaves them zero again (also one
+ *                  in which a row stalled).  So a workspace zero-filled once
+ *                  serves every later call with the same or fewer rows (any
+ *                  K, V).  Calls that may run concurrently need separate
+ *                  workspaces.
  * Errors: SPEC_ERR_INVALID_ARG, SPEC_ERR_WORKSPACE, SPEC_ERR_HIP.
  * B == 0 returns SPEC_OK without launching.
  * ---------------------------------------------------------------------- */
@@ -160,8 +159,10 @@ int spec_accept(const void* target_logits, int logits_dtype,
  * the kept mass.  top_p == 1 and min_p == 0 turn (a) and (b) off.  A draft
  * token outside q''s kept set makes the row invalid (SPEC_ROW_ZERO_Q).
  * out_p_draft holds p'_i(x_i).  Same uniforms, inverse-CDF rule, residual
- * fall-back and per-row status bits as spec_accept, plus the informational
- * SPEC_ROW_FILTER_COARSE.
+ * fall-back and per-row status bits as spec_accept.  The filters are
+ * resolved exactly: the top-p cut is the exact logit at which the mass,
+ * counted from the top in 2^-40 fixed point of fp32 weights, reaches top_p
+ * of the total.
  *
  * Arguments: as spec_accept, except
  *   draft_logits   [B, K, V] of logits_dtype (the same dtype as the target)
@@ -364,11 +365,24 @@ int spec_verify_attention(const void* q, const void* k_cache, const void* v_cach
                           int out_dtype, int32_t* out_status, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * spec_debug_set_wait_bound -- sets how many times a spec_accept workgroup
+ * polls its row's decision (a poll is two coherent loads and a short sleep,
+ * about 1.5 us) before it gives up on the row and reports SPEC_ROW_STALLED;
+ * polls == 0 restores the
+ * default (65536, about 0.1 s).  Process-wide, read by each later
+ * spec_accept call when it is enqueued.  It exists so that tests can drive
+ * the give-up path with every kernel still ending normally: with a bound of
+ * 1, workgroups that find no decision on their first poll give up.
+ * Returns SPEC_OK, or SPEC_ERR_INVALID_ARG for polls < 0.
+ * ---------------------------------------------------------------------- */
+int spec_debug_set_wait_bound(int polls);
+
 /* Human-readable text of a return code (static storage). */
 const char* spec_status_string(int code);
 
 /* ABI version of this header (incremented on incompatible changes). */
-#define SPEC_VERIFY_ABI_VERSION 2
+#define SPEC_VERIFY_ABI_VERSION 3
 int spec_abi_version(void);
 
 #ifdef __cplusplus

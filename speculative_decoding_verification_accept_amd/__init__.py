@@ -38,7 +38,6 @@ ROW_BAD_LEN = 4
 ROW_ZERO_Q = 8
 ROW_RESID_ZERO = 16
 ROW_STALLED = 32
-ROW_FILTER_COARSE = 64
 MAX_DRAFT = 255
 ADAPT_MAX_K = 32
 ADAPT_STATE_BYTES = 64
@@ -76,6 +75,7 @@ ABI = [
     ("spec_plan_depth", ctypes.c_int,
      [_P, _P, ctypes.c_int, _P, ctypes.c_int, ctypes.c_int, ctypes.c_double, ctypes.c_double,
       _P, _P, _P, _P]),
+    ("spec_debug_set_wait_bound", ctypes.c_int, [ctypes.c_int]),
     ("spec_status_string", ctypes.c_char_p, [ctypes.c_int]),
     ("spec_abi_version", ctypes.c_int, []),
 ]
@@ -109,6 +109,15 @@ def load_library():
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+def set_wait_bound(polls: int) -> None:
+    """Polls of a row's decision before a spec_accept workgroup gives up
+    (``spec_debug_set_wait_bound``; 0 restores the default).  For tests of
+    the give-up path."""
+    rc = load_library().spec_debug_set_wait_bound(int(polls))
+    if rc != SPEC_OK:
+        raise SpecError("spec_debug_set_wait_bound", rc)
 
 
 def status_string(code: int) -> str:

@@ -64,6 +64,8 @@
 
 #include <math.h>
 
+#include <atomic>
+
 namespace specv {
 namespace {
 
@@ -77,15 +79,16 @@ constexpr int kMinChunk = kChunkBytes / 4;   // the smallest chunk (fp32), for s
 constexpr int kPos = SPEC_MAX_DRAFT + 1;     // positions per row at most
 constexpr int kMaxChunks = 1024;             // chunks per row at most (the sampler keeps their masses in LDS)
 constexpr int kMergeRegs = 2;                // chunk partials held per lane by the merge
-constexpr int kSpinLimit = 1 << 16;          // polls of one wait (~0.1 s) before giving up
+constexpr int kSpinLimit = 1 << 16;          // polls of one wait (~0.1 s) before giving up (default)
 constexpr int kRowStride = 64;               // ints per row-counter record: 256 bytes
 constexpr int kInvalidMask = SPEC_ROW_NONFINITE | SPEC_ROW_BAD_TOKEN | SPEC_ROW_BAD_LEN | SPEC_ROW_ZERO_Q;
 
 typedef uint16_t bf16_t;
 
 // Row-counter record (zero between calls): [0] phase-1 arrivals,
-// [16] phase-2 arrivals, [32..35] the two tagged decision words.
-constexpr int kCnt1 = 0, kCnt2 = 16, kDec = 32;
+// [16] phase-2 arrivals, [32..35] the two tagged decision words, [48] set by
+// a workgroup that gave up waiting for the decision.
+constexpr int kCnt1 = 0, kCnt2 = 16, kDec = 32, kStall = 48;
 
 // ---- exchange between workgroups -----------------------------------------------
 __device__ __forceinline__ void co_store(uint64_t* p, uint64_t v) {
@@ -96,6 +99,9 @@ __device__ __forceinline__ uint64_t co_load(const uint64_t* p) {
 }
 __device__ __forceinline__ void co_store32(int* p, int v) {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int co_load32(const int* p) {
+    return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ int co_add(int* p, int v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -503,6 +509,7 @@ struct Args {
     const int32_t* lens;
     int64_t B, V, row_base;
     int K, C;
+    int spin_limit;  // polls of the decision before a workgroup gives up on its row
     float c;  // log2(e) / T (stochastic)
     uint64_t seed, offset;
     int32_t* out_tokens;
@@ -807,7 +814,7 @@ __global__ __launch_bounds__(kThreads) void k_accept(Args g) {
                 w0 = co_load(dw);
                 w1 = co_load(dw + 1);
                 if (w0 & w1 & 1) break;
-                if (++n >= kSpinLimit) break;
+                if (++n >= g.spin_limit) break;
                 __builtin_amdgcn_s_sleep(8);
             }
             sh.w0 = w0;
@@ -815,13 +822,10 @@ __global__ __launch_bounds__(kThreads) void k_accept(Args g) {
         }
     }
     __syncthreads();
-    if (!(sh.w0 & sh.w1 & 1)) {  // the bound ran out: give up on the row
-        if (t == 0) {
-            g.out_accepted[b] = -1;
-            if (g.out_status) g.out_status[b] = SPEC_ROW_STALLED;
-        }
-        return;
-    }
+    // The bound ran out: this workgroup gives up on the row.  It flags the
+    // row record and still counts in below, so the row's last workgroup
+    // (which writes the row as stalled) resets the record as always.
+    const bool stalled = !(sh.w0 & sh.w1 & 1);
     const Decision d = dec_read(sh.w0, sh.w1);
     const bool invalid = (d.status & kInvalidMask) != 0;
     const int a = d.a;
@@ -835,12 +839,14 @@ __global__ __launch_bounds__(kThreads) void k_accept(Args g) {
     const float* qrow = d.reject ? g.q + (b * K + a) * V : nullptr;
     uint64_t* tsrow = g.tsum + b * C * kThreads;  // [C][kThreads]
     double mass = 0.0;
-    if (!invalid) {
+    if (stalled) {
+        if (t == 0) co_store32(rowc + kStall, 1);
+    } else if (!invalid) {
         const double own = thread_weight_sum<T, VEC, EPT>(zrow, qrow, V, chunk0 + (int64_t)t * EPT, c, mcM, d.invS);
         co_store(tsrow + (int64_t)ci * kThreads + t, dbits(own));
         mass = block_sum(own, sh.red_d);
     }
-    if (t == 0) co_store(g.mass + b * C + ci, dbits(mass));
+    if (t == 0 && !stalled) co_store(g.mass + b * C + ci, dbits(mass));
     drain_vm();
     __syncthreads();
     if (t == 0) sh.last = (co_add(rowc + kCnt2, 1) == C - 1);
@@ -849,11 +855,24 @@ __global__ __launch_bounds__(kThreads) void k_accept(Args g) {
 
     // ---- sample (the row's last workgroup) ----
     // Every workgroup of the row has counted in, so none reads the row's
-    // record again: reset it for the next call.
+    // record again: reset it for the next call.  A workgroup that gave up
+    // flagged the record before counting in; the row is then written as
+    // stalled (the decider may never have finished it).
     if (t == 0) {
+        sh.last = co_load32(rowc + kStall);
         co_store32(rowc + kCnt2, 0);
+        co_store32(rowc + kStall, 0);
         co_store(reinterpret_cast<uint64_t*>(rowc + kDec), 0);
         co_store(reinterpret_cast<uint64_t*>(rowc + kDec) + 1, 0);
+    }
+    __syncthreads();
+    if (sh.last != 0) {
+        for (int i = t; i <= K; i += kThreads) g.out_tokens[b * (K + 1) + i] = -1;
+        if (t == 0) {
+            g.out_accepted[b] = -1;
+            if (g.out_status) g.out_status[b] = SPEC_ROW_STALLED;
+        }
+        return;
     }
     if (invalid) return;  // the decider wrote the row
     int status = d.status;
@@ -979,6 +998,10 @@ int launch_accept(const Args& a, hipStream_t stream, bool greedy) {
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Polls of the decision before a workgroup gives up on its row (process-wide;
+// only a test of the give-up path changes it).
+std::atomic<int> g_wait_bound{kSpinLimit};
+
 }  // namespace
 }  // namespace specv
 
@@ -1022,6 +1045,7 @@ extern "C" int spec_accept(const void* target_logits, int logits_dtype, const fl
     a.row_base = row_base;
     a.K = K;
     a.C = (int)C;
+    a.spin_limit = g_wait_bound.load(std::memory_order_relaxed);
     // c = log2(e) / T, rounded once to fp32
     a.c = greedy ? 0.f : (float)(1.4426950408889634074 / (double)temperature);
     a.seed = philox_seed;
@@ -1042,4 +1066,10 @@ extern "C" int spec_accept(const void* target_logits, int logits_dtype, const fl
     }
     const bool vec = (V % 4 == 0) && aligned16(target_logits) && (!a.q || aligned16(a.q));
     return vec ? launch_accept<float, true>(a, s, greedy) : launch_accept<float, false>(a, s, greedy);
+}
+
+extern "C" int spec_debug_set_wait_bound(int polls) {
+    if (polls < 0) return SPEC_ERR_INVALID_ARG;
+    g_wait_bound.store(polls == 0 ? kSpinLimit : polls, std::memory_order_relaxed);
+    return SPEC_OK;
 }

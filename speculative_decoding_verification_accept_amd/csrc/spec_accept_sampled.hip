@@ -32,8 +32,10 @@
 //            of 8 bits, fixed-point mass histograms) finds the exact logit
 //            at which the mass reaches top_p: kept iff key(z) >= that key.
 //            Pass 3: the kept mass S' = sum of kept e in fp64, in a fixed
-//            order.  A crossing bin of more than 4096 entries keeps the
-//            whole bin and sets SPEC_ROW_FILTER_COARSE.
+//            order.  A crossing bin of more than 4096 entries (or a cut in
+//            the unbinned tail past u = 32) is resolved by the same radix
+//            select with each digit's histogram taken by one more pass over
+//            the row.
 //            With min-p on, one pass instead: the max, the total mass (each
 //            thread's fp64 sum relative to a power of two at least its
 //            reference max, rescaled exactly as the reference grows; the
@@ -127,7 +129,6 @@ struct Stat {
     uint32_t tau;   // kept iff fkey(z) >= tau (0: no top-p)
     double s;       // kept mass sum of e
     int flag;       // 1: NaN / +Inf / all -Inf
-    int coarse;     // the top-p crossing bin was kept whole
 };
 
 struct Args {
@@ -175,7 +176,7 @@ struct StatShared {
     float red_f[kWS];
     int red_i[kWS];
     int ncand, bstar;
-    uint32_t prefix, kmin, mrun;
+    uint32_t prefix, mrun;
     double rem;
 };
 
@@ -273,14 +274,17 @@ __device__ __forceinline__ void row_rounds(const T* row, int64_t V, F&& f) {
     if constexpr (VEC) {
         constexpr int W = VecRound<T>::W;
         const int64_t nv = V / W;
-        // buffer loads: a 32-bit offset per lane, the round's step in the
-        // scalar offset, and reads past the row's end return zeros
+        // buffer loads over the row: the whole byte offset is the per-lane
+        // offset (the hardware's range check covers it, not the scalar
+        // offset), so reads past the row's end return zeros and never leave
+        // the row.  A row holds at most 16 MiB (kMaxChunks chunks), so
+        // offsets up to a round past its end fit in 32 bits.
         typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc((void*)row, (short)0, (int)(nv * 16), 0x00020000);
         constexpr int64_t kStep = (int64_t)kTS * kU;
         auto ld16 = [&](int64_t v) -> uint4 {
-            const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(t * 16), (int)(v * 16), 0);
+            const u32x4 r = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)((v + t) * 16), 0, 0);
             return make_uint4(r.x, r.y, r.z, r.w);
         };
         VecRound<T> z, nz;
@@ -628,9 +632,12 @@ __global__ __launch_bounds__(kTS) void k_stats(Args a) {
         });
         const unsigned long long S = block_sum_u64(tot, sh);
         if (t == 0) {
+            // the crossing bin: the first (from the top) whose cumulative
+            // mass reaches need; past the last bin, the unbinned tail
+            // (u >= 32), where the rest of the mass lies
             const double need = (double)a.top_p * (double)S;
             unsigned long long acc = 0ull;
-            int bs = kBins - 1;
+            int bs = kBins;
             for (int k = 0; k < kBins; ++k) {
                 if ((double)(acc + sh.hm[k]) >= need) {
                     bs = k;
@@ -641,21 +648,24 @@ __global__ __launch_bounds__(kTS) void k_stats(Args a) {
             sh.bstar = bs;
             sh.rem = need - (double)acc;  // > 0: mass still needed inside the bin
             sh.ncand = 0;
-            sh.kmin = 0xFFFFFFFFu;
         }
         __syncthreads();
         const int bs = sh.bstar;
         const double rem = sh.rem;
-        const bool fits = sh.hc[bs] <= (uint32_t)kCand;
+        const bool fits = bs < kBins && sh.hc[bs] <= (uint32_t)kCand;
         __syncthreads();  // the entries below overwrite the histogram
-        // collect the crossing bin's entries (or only their smallest key)
-        row_pass<T, VEC>(row, V, [&](float z, int64_t, bool ok) {
-            const float w = __builtin_fmaf(z, c, -mc);
-            const unsigned long long q = ok ? (unsigned long long)(hw_exp2(w) * kFix40) : 0ull;
-            const float u = -w;
-            const bool in = q && u < 32.f && (int)(u * kBinScale) == bs;
-            const uint32_t key = fkey(z);
-            if (fits) {
+        // in the crossing bin: a positive mass and u in the bin (every entry
+        // of a higher bin has a strictly larger logit, and equal logits
+        // share a bin)
+        auto in_bin = [bs](float u, unsigned long long q) {
+            return q && (bs < kBins ? (u < 32.f && (int)(u * kBinScale) == bs) : !(u < 32.f));
+        };
+        if (fits) {
+            // collect the crossing bin's entries in LDS, then radix-select there
+            row_pass<T, VEC>(row, V, [&](float z, int64_t, bool ok) {
+                const float w = __builtin_fmaf(z, c, -mc);
+                const unsigned long long q = ok ? (unsigned long long)(hw_exp2(w) * kFix40) : 0ull;
+                const bool in = in_bin(-w, q);
                 const uint64_t mask = __ballot(in);
                 if (mask) {
                     int base = 0;
@@ -663,20 +673,47 @@ __global__ __launch_bounds__(kTS) void k_stats(Args a) {
                     base = __shfl(base, 0, kWave);
                     if (in) {
                         const int slot = base + __popcll(mask & ((1ull << lane) - 1ull));
-                        sh.ck[slot] = key;
+                        sh.ck[slot] = fkey(z);
                         sh.cq[slot] = q;
                     }
                 }
-            } else if (in) {
-                atomicMin(&sh.kmin, key);
-            }
-        });
-        __syncthreads();
-        if (fits) {
+            });
+            __syncthreads();
             tau = radix_cut(sh, sh.ncand, rem);
         } else {
-            tau = sh.kmin;
-            st.coarse = 1;
+            // more entries than LDS holds (or the tail): the same radix
+            // select, each 8-bit digit from one more pass over the row.  A
+            // thread adds a run of equal digits to the LDS histogram at once.
+            uint32_t prefix = 0;
+            double r = rem;
+            for (int lvl = 0; lvl < 4; ++lvl) {
+                const int shift = 24 - 8 * lvl;
+                if (t < 256) sh.dig[t] = 0ull;
+                __syncthreads();
+                uint32_t run_d = 0xFFFFFFFFu;
+                unsigned long long run_q = 0ull;
+                row_pass<T, VEC>(row, V, [&](float z, int64_t, bool ok) {
+                    const float w = __builtin_fmaf(z, c, -mc);
+                    const unsigned long long q = ok ? (unsigned long long)(hw_exp2(w) * kFix40) : 0ull;
+                    const uint32_t key = fkey(z);
+                    if (in_bin(-w, q) && (lvl == 0 || (key >> (shift + 8)) == prefix)) {
+                        const uint32_t d = (key >> shift) & 255u;
+                        if (d != run_d) {
+                            if (run_q) atomicAdd(&sh.dig[run_d], run_q);
+                            run_d = d;
+                            run_q = 0ull;
+                        }
+                        run_q += q;
+                    }
+                });
+                if (run_q) atomicAdd(&sh.dig[run_d], run_q);
+                __syncthreads();
+                pick_digit(sh.dig, r, prefix, sh.red_u, sh.red_i, &sh.prefix, &sh.rem);
+                __syncthreads();
+                prefix = sh.prefix;
+                r = sh.rem;
+            }
+            tau = prefix;
         }
     }
 
@@ -874,8 +911,6 @@ __global__ __launch_bounds__(kT) void k_accept(Args a) {
         }
         return;
     }
-    for (int i = 0; i < L + 1; ++i) status |= stb[i].coarse ? SPEC_ROW_FILTER_COARSE : 0;
-    for (int i = 0; i < L; ++i) status |= stb[K + 1 + i].coarse ? SPEC_ROW_FILTER_COARSE : 0;
 
     // phase 2: this chunk's draw weights at position ar
     const bool reject = ar < L;

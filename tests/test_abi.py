@@ -34,14 +34,15 @@ def test_header_declares_the_boundary():
                           "spec_abi_version", "spec_adapt", "spec_adapt_state_bytes",
                           "spec_adapt_telemetry_bytes", "spec_plan_depth",
                           "spec_verify_attention", "spec_verify_attention_workspace_bytes",
-                          "spec_accept_sampled", "spec_accept_sampled_workspace_bytes"]), fns
+                          "spec_accept_sampled", "spec_accept_sampled_workspace_bytes",
+                          "spec_debug_set_wait_bound"]), fns
     assert sorted(n for n, _, _ in sv.ABI) == fns
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.spec_abi_version() == 2
+    assert lib.spec_abi_version() == 3
     assert sv.status_string(0) == "ok"
     assert "invalid" in sv.status_string(-1)
 
@@ -235,3 +236,10 @@ def test_accept_sampled_argument_validation(lib):
     assert _sampled(lib, B=0) == sv.SPEC_OK
     n = lib.spec_accept_sampled_workspace_bytes(64, 7, 128256)
     assert n >= 64 * 256 + 64 * 15 * 32
+
+
+def test_wait_bound_control(lib):
+    # host-only: the give-up bound of spec_accept's waits
+    assert lib.spec_debug_set_wait_bound(-1) == sv.SPEC_ERR_INVALID_ARG
+    assert lib.spec_debug_set_wait_bound(5) == sv.SPEC_OK
+    assert lib.spec_debug_set_wait_bound(0) == sv.SPEC_OK

@@ -232,3 +232,41 @@ def test_draft_equal_to_target():
     g, o = run_pair(inp, label="draft == target")
     compare(g, o, K, label="draft == target")
     assert (g["accepted"] == K).mean() > 0.99
+
+
+def test_give_up_path_leaves_the_workspace_valid():
+    # A wait bound of one poll makes most workgroups give up on their row's
+    # decision (every kernel still ends normally).  Stalled rows report
+    # ROW_STALLED with -1 outputs, every other row matches the oracle, the
+    # row records are zero afterwards, and the next call on the same
+    # workspace is exact again.
+    inp = workloads.accept_inputs(48, 5, 60000, logit_std=3.0, draft_noise=1.0, temperature=0.8,
+                                  seed=44, bf16=True, ragged=True)
+    z, q = inp.logits.cuda(), _dev(inp.draft_probs)
+    x, L = _dev(inp.draft_tokens), _dev(inp.draft_lens)
+    B, K = inp.B, inp.K
+    ws = sv.accept_workspace(B, K, inp.V, z.device)
+    print("[spec_accept] give-up path: wait bound 1 poll", flush=True)
+    sv.set_wait_bound(1)
+    try:
+        got = gpu_to_numpy(sv.accept(z, q, x, L, temperature=0.8, seed=inp.seed, offset=3,
+                                     workspace=ws))
+    finally:
+        sv.set_wait_bound(0)
+    assert torch.count_nonzero(ws[:256 * B]).item() == 0, "row records not reset"
+    o = oracle.spec_accept(inp.logits_f32(), inp.draft_probs, inp.draft_tokens, inp.draft_lens,
+                           0.8, inp.seed, 3, nthreads=NTHREADS)
+    stalled = got["status"] == sv.ROW_STALLED
+    print(f"{int(stalled.sum())} of {B} rows stalled")
+    assert stalled.any()
+    assert np.all(got["accepted"][stalled] == -1) and np.all(got["tokens"][stalled] == -1)
+    keep = ~stalled
+    sub = {k: v[keep] for k, v in got.items()}
+    osub = {k: v[keep] for k, v in o.items()}
+    compare(sub, osub, K, label="rows that did not stall")
+    # the same workspace, default bound: every row exact
+    print("[spec_accept] give-up path: default bound on the same workspace", flush=True)
+    g2 = gpu_to_numpy(sv.accept(z, q, x, L, temperature=0.8, seed=inp.seed, offset=3, workspace=ws))
+    assert not np.any(g2["status"] == sv.ROW_STALLED)
+    compare(g2, o, K, label="after a stalled call")
+    assert torch.count_nonzero(ws[:256 * B]).item() == 0
