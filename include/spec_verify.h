@@ -23,7 +23,8 @@
  *    (spec_plan_depth alone takes host arrays).
  *    The library allocates nothing and keeps no state between calls, so
  *    calls on different streams may run concurrently provided their
- *    workspaces do not overlap.
+ *    workspaces do not overlap (spec_accept_noalloc alone uses a static
+ *    device array of its own; see there).
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Calls enqueue work on it and return; outputs are valid once the stream
  *    has synchronised.
@@ -138,6 +139,33 @@ int spec_accept(const void* target_logits, int logits_dtype,
                 uint64_t philox_offset, int32_t* out_tokens, int32_t* out_accepted,
                 float* out_p_draft, int32_t* out_status, void* workspace,
                 size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * spec_accept_noalloc -- spec_accept for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation, arguments and outputs, with no
+ * workspace argument.
+ *
+ * The workspace is a static device array of 16 MiB inside the library, one
+ * per GPU, held until the process ends.  On the first call on a device the
+ * library takes the array's device address (hipGetSymbolAddress) and clears
+ * it with a kernel on `stream`; no call allocates or frees memory.  A call
+ * whose workspace, spec_accept_workspace_bytes(B, K, V), exceeds 16 MiB
+ * returns SPEC_ERR_WORKSPACE before any launch (the fused step's B = 32,
+ * K = 5, V = 151936 needs 2.5 MiB; B = 64, K = 7, V = 128256 needs 4.3 MiB).
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or host threads) race and give wrong results;
+ * order them on one stream.  Each call leaves the array's row records zero,
+ * as the next call needs them.
+ * Errors: as spec_accept, plus SPEC_ERR_HIP if the array's address cannot
+ * be obtained.
+ * ---------------------------------------------------------------------- */
+int spec_accept_noalloc(const void* target_logits, int logits_dtype,
+                        const float* draft_probs, const int32_t* draft_tokens,
+                        const int32_t* draft_lens, int64_t B, int K, int64_t V,
+                        int64_t row_base, float temperature, uint64_t philox_seed,
+                        uint64_t philox_offset, int32_t* out_tokens, int32_t* out_accepted,
+                        float* out_p_draft, int32_t* out_status, void* stream);
 
 /* ------------------------------------------------------------------------
  * spec_accept_sampled -- accept/reject with the production sampler's

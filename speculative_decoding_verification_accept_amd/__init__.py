@@ -54,6 +54,9 @@ ABI = [
     ("spec_accept", ctypes.c_int,
      [_P, ctypes.c_int, _P, _P, _P, _I64, ctypes.c_int, _I64, _I64, ctypes.c_float, _U64, _U64,
       _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    ("spec_accept_noalloc", ctypes.c_int,
+     [_P, ctypes.c_int, _P, _P, _P, _I64, ctypes.c_int, _I64, _I64, ctypes.c_float, _U64, _U64,
+      _P, _P, _P, _P, _P]),
     ("spec_accept_sampled_workspace_bytes", ctypes.c_size_t, [_I64, ctypes.c_int, _I64]),
     ("spec_accept_sampled", ctypes.c_int,
      [_P, _P, ctypes.c_int, _P, _P, _I64, ctypes.c_int, _I64, _I64, ctypes.c_float,

@@ -65,6 +65,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <mutex>
 
 namespace specv {
 namespace {
@@ -998,6 +999,8 @@ int launch_accept(const Args& a, hipStream_t stream, bool greedy) {
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+constexpr int kMaxDevicesNoAlloc = 64;  // devices the allocation-free entry point serves
+
 // Polls of the decision before a workgroup gives up on its row (process-wide;
 // only a test of the give-up path changes it).
 std::atomic<int> g_wait_bound{kSpinLimit};
@@ -1012,30 +1015,41 @@ extern "C" size_t spec_accept_workspace_bytes(int64_t B, int K, int64_t V) {
     return accept_ws_layout(B, K, V).total;
 }
 
-extern "C" int spec_accept(const void* target_logits, int logits_dtype, const float* draft_probs,
-                           const int32_t* draft_tokens, const int32_t* draft_lens, int64_t B,
-                           int K, int64_t V, int64_t row_base, float temperature,
-                           uint64_t philox_seed, uint64_t philox_offset, int32_t* out_tokens,
-                           int32_t* out_accepted, float* out_p_draft, int32_t* out_status,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+namespace specv {
+namespace {
+
+// Host-side validation and argument packing shared by the entry points.
+// Returns SPEC_OK with the call packed, kNothing when B == 0, or a negative
+// code; it makes no HIP call.
+constexpr int kNothing = 1;
+struct AcceptCall {
+    Args a;
+    AcceptWs lay;
+    bool bf16, greedy, vec;
+};
+
+int accept_prepare(const void* target_logits, int logits_dtype, const float* draft_probs,
+                   const int32_t* draft_tokens, const int32_t* draft_lens, int64_t B, int K,
+                   int64_t V, int64_t row_base, float temperature, uint64_t philox_seed,
+                   uint64_t philox_offset, int32_t* out_tokens, int32_t* out_accepted,
+                   float* out_p_draft, int32_t* out_status, AcceptCall& call) {
     if (B < 0 || K < 0 || K > SPEC_MAX_DRAFT || V < 1 || V > 0x7FFFFFFF || row_base < 0)
         return SPEC_ERR_INVALID_ARG;
     if (row_base + B > ((int64_t)1 << 32)) return SPEC_ERR_INVALID_ARG;
     if (logits_dtype != SPEC_F32 && logits_dtype != SPEC_BF16) return SPEC_ERR_INVALID_ARG;
     if (!(temperature >= 0.f) || isinf(temperature)) return SPEC_ERR_INVALID_ARG;
-    if (B == 0) return SPEC_OK;
+    if (B == 0) return kNothing;
     if (!target_logits || !out_tokens || !out_accepted) return SPEC_ERR_INVALID_ARG;
     if (K > 0 && !draft_tokens) return SPEC_ERR_INVALID_ARG;
     if (temperature > 0.f && K > 0 && !draft_probs) return SPEC_ERR_INVALID_ARG;
-    const int64_t C = logits_dtype == SPEC_BF16 ? (V + chunk_of<bf16_t>() - 1) / chunk_of<bf16_t>()
-                                                : (V + chunk_of<float>() - 1) / chunk_of<float>();
+    const bool bf16 = logits_dtype == SPEC_BF16;
+    const int64_t C = bf16 ? (V + chunk_of<bf16_t>() - 1) / chunk_of<bf16_t>()
+                           : (V + chunk_of<float>() - 1) / chunk_of<float>();
     // one workgroup per (row, chunk); the sampler holds a row's chunk masses in LDS
     if (B * C > ((int64_t)1 << 24) || C > kMaxChunks) return SPEC_ERR_INVALID_ARG;
-    const AcceptWs lay = accept_ws_layout(B, K, V);
-    if (!workspace || workspace_bytes < lay.total || !aligned16(workspace)) return SPEC_ERR_WORKSPACE;
-    char* ws = static_cast<char*>(workspace);
     const bool greedy = temperature == 0.f;
-    Args a{};
+    Args& a = call.a;
+    a = Args{};
     a.logits = target_logits;
     a.q = greedy ? nullptr : draft_probs;
     a.tokens = draft_tokens;
@@ -1054,18 +1068,107 @@ extern "C" int spec_accept(const void* target_logits, int logits_dtype, const fl
     a.out_accepted = out_accepted;
     a.out_p_draft = out_p_draft;
     a.out_status = out_status;
+    call.lay = accept_ws_layout(B, K, V);
+    call.bf16 = bf16;
+    call.greedy = greedy;
+    call.vec = (V % (bf16 ? 8 : 4) == 0) && aligned16(target_logits) && (!a.q || aligned16(a.q));
+    return SPEC_OK;
+}
+
+// Points the call at its workspace `ws` (device memory of call.lay.total
+// bytes whose row records are zero) and launches it on `s`.
+int accept_launch(AcceptCall& call, char* ws, hipStream_t s) {
+    Args& a = call.a;
+    const AcceptWs& lay = call.lay;
     a.rows = reinterpret_cast<int*>(ws + lay.rows_off);
     a.part = reinterpret_cast<uint64_t*>(ws + lay.part_off);
     a.gath = reinterpret_cast<uint64_t*>(ws + lay.gath_off);
     a.mass = reinterpret_cast<uint64_t*>(ws + lay.mass_off);
     a.tsum = reinterpret_cast<uint64_t*>(ws + lay.tsum_off);
+    if (call.bf16)
+        return call.vec ? launch_accept<bf16_t, true>(a, s, call.greedy) : launch_accept<bf16_t, false>(a, s, call.greedy);
+    return call.vec ? launch_accept<float, true>(a, s, call.greedy) : launch_accept<float, false>(a, s, call.greedy);
+}
+
+}  // namespace
+}  // namespace specv
+
+extern "C" int spec_accept(const void* target_logits, int logits_dtype, const float* draft_probs,
+                           const int32_t* draft_tokens, const int32_t* draft_lens, int64_t B,
+                           int K, int64_t V, int64_t row_base, float temperature,
+                           uint64_t philox_seed, uint64_t philox_offset, int32_t* out_tokens,
+                           int32_t* out_accepted, float* out_p_draft, int32_t* out_status,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    AcceptCall call;
+    const int rc = accept_prepare(target_logits, logits_dtype, draft_probs, draft_tokens, draft_lens, B, K, V,
+                                  row_base, temperature, philox_seed, philox_offset, out_tokens, out_accepted,
+                                  out_p_draft, out_status, call);
+    if (rc == kNothing) return SPEC_OK;
+    if (rc != SPEC_OK) return rc;
+    if (!workspace || workspace_bytes < call.lay.total || !aligned16(workspace)) return SPEC_ERR_WORKSPACE;
+    return accept_launch(call, static_cast<char*>(workspace), reinterpret_cast<hipStream_t>(stream));
+}
+
+// ---- the entry point that allocates nothing -------------------------------------------
+// Its workspace is this file-scope array, one copy per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device memory: the device address comes from hipGetSymbolAddress, once per
+// device with that device current, and only that address is ever passed on.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace specv {
+namespace {
+
+__global__ void k_zero16(uint4* p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+struct ScratchDev {
+    std::mutex mu;
+    char* ptr = nullptr;  // device address of `scratch` on this device, once set up
+};
+ScratchDev g_scratch[kMaxDevicesNoAlloc];
+
+// The current device's copy of `scratch`; on first use, its address is taken
+// and the whole array is cleared by a fill kernel on `s` (the row records must
+// start at zero; every call leaves them zero).  Null on a HIP error.
+char* scratch_of_current_device(hipStream_t s) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevicesNoAlloc) return nullptr;
+    ScratchDev& sd = g_scratch[dev];
+    std::lock_guard<std::mutex> lock(sd.mu);
+    if (sd.ptr) return sd.ptr;
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    hipLaunchKernelGGL(k_zero16, dim3(1024), dim3(256), 0, s, static_cast<uint4*>(p),
+                       (int64_t)(kScratchBytes / sizeof(uint4)));
+    if (hipGetLastError() != hipSuccess) return nullptr;
+    sd.ptr = static_cast<char*>(p);
+    return sd.ptr;
+}
+
+}  // namespace
+}  // namespace specv
+
+extern "C" int spec_accept_noalloc(const void* target_logits, int logits_dtype, const float* draft_probs,
+                                   const int32_t* draft_tokens, const int32_t* draft_lens, int64_t B,
+                                   int K, int64_t V, int64_t row_base, float temperature,
+                                   uint64_t philox_seed, uint64_t philox_offset, int32_t* out_tokens,
+                                   int32_t* out_accepted, float* out_p_draft, int32_t* out_status,
+                                   void* stream) {
+    AcceptCall call;
+    const int rc = accept_prepare(target_logits, logits_dtype, draft_probs, draft_tokens, draft_lens, B, K, V,
+                                  row_base, temperature, philox_seed, philox_offset, out_tokens, out_accepted,
+                                  out_p_draft, out_status, call);
+    if (rc == kNothing) return SPEC_OK;
+    if (rc != SPEC_OK) return rc;
+    if (call.lay.total > kScratchBytes) return SPEC_ERR_WORKSPACE;
     const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    if (logits_dtype == SPEC_BF16) {
-        const bool vec = (V % 8 == 0) && aligned16(target_logits) && (!a.q || aligned16(a.q));
-        return vec ? launch_accept<bf16_t, true>(a, s, greedy) : launch_accept<bf16_t, false>(a, s, greedy);
-    }
-    const bool vec = (V % 4 == 0) && aligned16(target_logits) && (!a.q || aligned16(a.q));
-    return vec ? launch_accept<float, true>(a, s, greedy) : launch_accept<float, false>(a, s, greedy);
+    char* ws = scratch_of_current_device(s);
+    if (!ws) return SPEC_ERR_HIP;
+    return accept_launch(call, ws, s);
 }
 
 extern "C" int spec_debug_set_wait_bound(int polls) {

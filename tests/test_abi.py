@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
                           "spec_adapt_telemetry_bytes", "spec_plan_depth",
                           "spec_verify_attention", "spec_verify_attention_workspace_bytes",
                           "spec_accept_sampled", "spec_accept_sampled_workspace_bytes",
-                          "spec_debug_set_wait_bound"]), fns
+                          "spec_debug_set_wait_bound", "spec_accept_noalloc"]), fns
     assert sorted(n for n, _, _ in sv.ABI) == fns
 
 
