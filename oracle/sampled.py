@@ -30,6 +30,12 @@ Readings taken where the pages are silent:
     computed on the tempered, unfiltered distribution; a token is kept iff
     both keep it; the kept probabilities are renormalised.  top_p >= 1 and
     min_p <= 0 disable the respective filter.
+  * The listing stops at the first rejection, so the target's distribution
+    at position i is read only when every draft before it was accepted (the
+    bonus position L only when all were): a non-finite target position makes
+    the row invalid only if it is read, and p'_i(x_i) is reported for the
+    tested positions only.  The drafted tokens are validated for all L
+    drafts (range, finite draft logits, token in q''s kept set).
   * The target's filtered distribution p' and the draft's q' (with the
     draft's own temperature) replace p and q in the acceptance rule,
     residual and bonus draw of the unfiltered pass, with the same uniforms,
@@ -76,6 +82,27 @@ def filtered(z, T: float, top_p: float, min_p: float):
     return pk / pk.sum(), keep, near, False
 
 
+def near_tokens(z, T: float, top_p: float, min_p: float):
+    """bool [V]: the tokens whose keep decision under the filters lies within
+    1e-6 of its threshold (their value's mass-above against top_p, or p_j /
+    max p against min_p); None for a non-finite position."""
+    z64 = np.asarray(z, dtype=np.float64)
+    if not np.all(np.isfinite(z64) | (z64 == -np.inf)) or np.all(z64 == -np.inf):
+        return None
+    m = z64.max()
+    e = np.exp((z64 - m) / T)
+    p = e / e.sum()
+    near = np.zeros(z64.shape[0], bool)
+    if top_p < 1.0:
+        vals, inv = np.unique(z64, return_inverse=True)
+        mass = np.bincount(inv, weights=p, minlength=vals.shape[0])
+        above = np.cumsum(mass[::-1])[::-1] - mass
+        near |= (np.abs(above - top_p) < NEAR)[inv]
+    if min_p > 0.0:
+        near |= np.abs(e - min_p) < NEAR * min_p
+    return near
+
+
 def _inv_cdf(w, u):
     """Smallest j whose inclusive prefix sum of w exceeds t = u * sum(w); the
     last positive j when rounding leaves none; `near` when t is within
@@ -99,8 +126,11 @@ def spec_accept_sampled(target_logits, draft_logits, draft_tokens, draft_lens, T
     inputs widen exactly), draft_tokens [B, K], draft_lens [B] or None.
     Temperatures, top_p and min_p are rounded to fp32 as the GPU receives
     them.  Returns tokens [B, K+1] (-1 padded), accepted [B] (-1 invalid),
-    p_draft [B, K] (p'_i(x_i), -1 elsewhere), status [B], near [B] (a
-    decision of the row lay within 1e-6 of its threshold)."""
+    p_draft [B, K] (p'_i(x_i) at the tested positions, -1 elsewhere), status
+    [B], near [B] (a decision the row's outcome depends on lay within 1e-6
+    of its threshold: a filter cut at a target position read or a draft
+    position tested, the kept-set test of a draft token, an acceptance test
+    or the draw)."""
     z = np.asarray(target_logits, dtype=np.float32)
     d = np.asarray(draft_logits, dtype=np.float32)
     B, K1, V = z.shape
@@ -117,39 +147,58 @@ def spec_accept_sampled(target_logits, draft_logits, draft_tokens, draft_lens, T
         if L < 0 or L > K:
             out["status"][b] = ROW_BAD_LEN
             continue
+        # the drafted tokens are validated for all L drafts: each draft
+        # distribution q'_i, the token's range, and the token in q''s kept set
         st = 0
-        ps, qs, nearrow = [], [], False
-        for i in range(L + 1):
-            pf, _, nr, bad = filtered(z[b, i], Tp, tp, mp)
-            st |= ROW_NONFINITE if bad else 0
-            ps.append(pf)
-            nearrow |= nr
+        qs, qnear = [], []
         for i in range(L):
             qf, _, nr, bad = filtered(d[b, i], Tq, tp, mp)
             st |= ROW_NONFINITE if bad else 0
             qs.append(qf)
-            nearrow |= nr
+            qnear.append(nr)
+        ztok = []   # whether the kept-set test of x_i lies near a filter cut
         for i in range(L):
             if not 0 <= x[b, i] < V:
                 st |= ROW_BAD_TOKEN
-            elif qs[i] is not None and not qs[i][x[b, i]] > 0.0:
-                st |= ROW_ZERO_Q
-        if st & (ROW_NONFINITE | ROW_BAD_TOKEN | ROW_ZERO_Q):
+            elif qs[i] is not None:
+                ztok.append(bool(near_tokens(d[b, i], Tq, tp, mp)[x[b, i]]))
+                if not qs[i][x[b, i]] > 0.0:
+                    st |= ROW_ZERO_Q
+        if st:
             out["status"][b] = st
-            out["near"][b] = nearrow
+            out["near"][b] = any(ztok)
             continue
+        # the target's distributions in the listing's order: position i only
+        # when every draft before it was accepted, position L (the bonus) only
+        # when all were; a non-finite position read this way makes the row
+        # invalid, positions after the stop are never read
         gr = row_base + b
-        for i in range(L):
-            out["p_draft"][b, i] = ps[i][x[b, i]]
-        a = L
-        for i in range(L):
-            px, qx = ps[i][x[b, i]], qs[i][x[b, i]]
+        a, nearrow, ps, bad = L, False, {}, False
+        for i in range(L + 1):
+            pf, _, nr, badp = filtered(z[b, i], Tp, tp, mp)
+            if badp:
+                bad = True
+                break
+            ps[i] = pf
+            nearrow |= nr
+            if i == L:
+                break
+            nearrow |= qnear[i]
+            px, qx = pf[x[b, i]], qs[i][x[b, i]]
+            out["p_draft"][b, i] = px
             acc = min(1.0, px / qx)
             ua, _ = _orc.uniforms(seed, offset, gr, i)
             nearrow |= abs(ua - acc) < NEAR
             if not ua < acc:
                 a = i
                 break
+        # drafts past the stop matter only through their kept-set test
+        nearrow |= any(ztok[a + 1:]) if not bad else any(ztok[i + 1:])
+        if bad:
+            out["p_draft"][b] = -1.0
+            out["status"][b] = ROW_NONFINITE
+            out["near"][b] = nearrow
+            continue
         _, us = _orc.uniforms(seed, offset, gr, a)
         if a < L:
             w = np.maximum(ps[a] - qs[a], 0.0)

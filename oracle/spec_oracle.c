@@ -239,7 +239,8 @@ static void do_row(const job_t* jb, int64_t b, double* e, double* w)
     const float* zrow = jb->logits + b * (int64_t)(K + 1) * V;
     const float* qrow = jb->draft_probs ? jb->draft_probs + b * (int64_t)K * V : NULL;
 
-    /* Step 1: validate the row. */
+    /* Step 1: validate the drafted tokens: the length, every token's range
+     * and (stochastic mode) q_i(x_i) > 0, for all L drafts. */
     int status = 0;
     int L = jb->draft_lens ? jb->draft_lens[b] : K;
     if (L < 0 || L > K) {
@@ -247,8 +248,6 @@ static void do_row(const job_t* jb, int64_t b, double* e, double* w)
     } else {
         for (int i = 0; i < L; ++i)
             if (x[i] < 0 || (int64_t)x[i] >= V) status |= ORC_ROW_BAD_TOKEN;
-        for (int i = 0; i <= L; ++i)
-            status |= check_position(zrow + (int64_t)i * V, V);
         if (!greedy)
             for (int i = 0; i < L; ++i)
                 if (x[i] >= 0 && (int64_t)x[i] < V) {
@@ -262,17 +261,30 @@ static void do_row(const job_t* jb, int64_t b, double* e, double* w)
     }
     const uint32_t grow = (uint32_t)(jb->row_base + b);
 
+    /* The target's distributions are read in the listing's order: position
+     * i only when every draft before it was accepted, and position L (the
+     * bonus) only when all L were [P1 listing: the loop breaks at the first
+     * rejection].  A position read this way must be finite: a NaN or +Inf
+     * logit, or all logits -Inf, makes the row invalid (ROW_NONFINITE);
+     * positions after the stop are never read. */
     if (greedy) {
         /* Greedy limit [P2 "Speculative decoding": keep the longest prefix the
          * target agrees with, then take the target's own token]. */
         int a = L;
-        for (int i = 0; i < L; ++i) {
+        for (int i = 0; i <= L; ++i) {
             const float* z = zrow + (int64_t)i * V;
+            if (check_position(z, V)) {
+                if (jb->out_p_draft)
+                    for (int k = 0; k < K; ++k) jb->out_p_draft[b * K + k] = -1.0;
+                if (jb->out_status) jb->out_status[b] = ORC_ROW_NONFINITE;
+                return;
+            }
+            if (i == L) break;
             int64_t g = 0;
             for (int64_t j = 1; j < V; ++j)
                 if ((double)z[j] > (double)z[g]) g = j;
             if (jb->out_p_draft) jb->out_p_draft[b * K + i] = (x[i] == g) ? 1.0 : 0.0;
-            if (x[i] != g && a == L) a = i;
+            if (x[i] != g) { a = i; break; }
         }
         const float* z = zrow + (int64_t)a * V;
         int64_t g = 0;
@@ -285,26 +297,26 @@ static void do_row(const job_t* jb, int64_t b, double* e, double* w)
         return;
     }
 
-    /* Step 2: p_i(x_i) at every drafted position. */
-    for (int i = 0; i < L; ++i) {
-        const float* z = zrow + (int64_t)i * V;
-        double m = pos_max(z, V);
-        double S = pos_exp(z, V, m, T, NULL);
-        double px = exp(((double)z[x[i]] - m) / T) / S;
-        if (jb->out_p_draft) jb->out_p_draft[b * K + i] = px;
-    }
-
-    /* Step 3: sequential acceptance tests, stopping at the first rejection
-     * [P1 listing: accept with probability min(1, p/q), else resample and
-     * stop the round; P2 "Speculative decoding": acceptance rule]. */
+    /* Steps 2 and 3: at each drafted position in turn, p_i(x_i) and the
+     * acceptance test, stopping at the first rejection [P1 listing: accept
+     * with probability min(1, p/q), else resample and stop the round; P2
+     * "Speculative decoding": acceptance rule]. */
     int a = L;
     int near_acc = -1;
-    for (int i = 0; i < L; ++i) {
+    for (int i = 0; i <= L; ++i) {
         const float* z = zrow + (int64_t)i * V;
+        if (check_position(z, V)) {
+            if (jb->out_p_draft)
+                for (int k = 0; k < K; ++k) jb->out_p_draft[b * K + k] = -1.0;
+            if (jb->out_status) jb->out_status[b] = ORC_ROW_NONFINITE;
+            return;
+        }
+        if (i == L) break;
         const float* q = qrow + (int64_t)i * V;
         double m = pos_max(z, V);
         double S = pos_exp(z, V, m, T, NULL);
         double px = exp(((double)z[x[i]] - m) / T) / S;
+        if (jb->out_p_draft) jb->out_p_draft[b * K + i] = px;
         double qx = (double)q[x[i]];
         double ratio = (g_mutation == 3) ? qx / px : px / qx;
         double acc = ratio < 1.0 ? ratio : 1.0;

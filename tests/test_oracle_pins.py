@@ -366,9 +366,11 @@ def test_accepted_length_bounds_ragged(oracle_mod):
         assert np.array_equal(out["tokens"][b, :a[b]], inp.draft_tokens[b, :a[b]])
         assert 0 <= out["tokens"][b, a[b]] < inp.V
         assert np.all(out["tokens"][b, a[b] + 1:] == -1)
-        # p_draft holds p_i(x_i) for i < L_b and -1 after
-        assert np.all(out["p_draft"][b, L[b]:] == -1)
-        assert np.all((out["p_draft"][b, :L[b]] >= 0) & (out["p_draft"][b, :L[b]] <= 1))
+        # p_draft holds p_i(x_i) at the tested positions i <= a_b (i < L_b)
+        # and -1 after: the listing stops at the first rejection
+        t = min(a[b] + 1, L[b])
+        assert np.all(out["p_draft"][b, t:] == -1)
+        assert np.all((out["p_draft"][b, :t] >= 0) & (out["p_draft"][b, :t] <= 1))
 
 
 def test_p_draft_matches_textbook_softmax(oracle_mod):
@@ -379,7 +381,9 @@ def test_p_draft_matches_textbook_softmax(oracle_mod):
                                  inp.temperature, inp.seed, 0)
     T = np.float64(np.float32(inp.temperature))
     for b in range(inp.B):
-        for i in range(inp.K):
+        tested = min(out["accepted"][b] + 1, inp.K)
+        assert tested >= 1
+        for i in range(tested):
             p = scipy.special.softmax(z[b, i].astype(np.float64) / T)
             assert out["p_draft"][b, i] == pytest.approx(p[inp.draft_tokens[b, i]], rel=1e-12)
 
@@ -427,6 +431,37 @@ def test_status_bits(oracle_mod):
     z[0, 2, 0] = np.nan
     out = O.spec_accept(z, q, x, np.array([1, 2, 2], np.int32), 1.0, 1, 0)
     assert list(out["status"]) == [0, 0, 0]
+
+
+def test_positions_after_the_first_rejection_are_not_read(oracle_mod):
+    """The listing stops at the first rejection: a non-finite logit after it
+    is never read (the row is valid), while one at or before it makes the
+    row invalid; p_i(x_i) is reported for the tested positions only."""
+    O = oracle_mod
+    z, q, x = _base(B=3, K=3, V=16)
+    # position 0: the draft token has all of q's mass but almost none of p's,
+    # so the test at position 0 rejects (u < ~e^-30 never happens)
+    for b in range(3):
+        z[b, 0, :] = 0.0
+        z[b, 0, 7] = -30.0
+        q[b, 0, :] = 0.0
+        q[b, 0, 7] = 1.0
+        x[b, 0] = 7
+    z[0, 1, 3] = np.nan           # after the rejection: not read
+    z[1, 3, 2] = np.inf           # after the rejection: not read
+    z[2, 0, 5] = np.nan           # at the rejected position: read
+    out = O.spec_accept(z, q, x, None, 1.0, 5, 0)
+    assert list(out["status"]) == [0, 0, O.ROW_NONFINITE]
+    assert list(out["accepted"]) == [0, 0, -1]
+    assert np.all(out["p_draft"][:2, 0] < 1e-12) and np.all(out["p_draft"][:2, 1:] == -1)
+    assert np.all(out["p_draft"][2] == -1)
+    # greedy: the same after the first disagreement with the argmax
+    xg = x.copy()
+    for b in range(3):
+        xg[b, 0] = 8                # not the argmax of position 0 (token 0 ties win)
+    out = O.spec_accept(z, None, xg, None, 0.0, 5, 0)
+    assert list(out["status"]) == [0, 0, O.ROW_NONFINITE]
+    assert list(out["accepted"]) == [0, 0, -1]
 
 
 def test_invalid_arguments(oracle_mod):

@@ -140,3 +140,22 @@ def test_output_follows_the_filtered_target(tp, mp):
     alpha = S.acceptance_overlap(p0, qf[0])
     acc0 = (out["accepted"] >= 1).mean()
     assert abs(acc0 - alpha) < 4 * np.sqrt(alpha * (1 - alpha) / rounds)
+
+
+def test_positions_after_the_first_rejection_are_not_read():
+    # the listing's break: a non-finite target logit after the first
+    # rejection is never read; at or before it, the row is invalid.  The
+    # draft side is validated for every drafted position.
+    V, K, T = 12, 3, 1.0
+    z = np.zeros((3, K + 1, V), np.float32)
+    d = np.zeros((3, K, V), np.float32)
+    z[:, 0, 5] = -40.0          # p'(5) ~ 0 at position 0 ...
+    d[:, 0, 5] = 40.0           # ... where q' puts all its mass on token 5
+    x = np.full((3, K), 5, np.int32)
+    z[0, 2, 1] = np.nan         # after the rejection at 0: not read
+    z[1, 0, 2] = np.inf         # at the rejected position: read
+    d[2, 2, 3] = np.nan         # a draft distribution: validated for all drafts
+    out = S.spec_accept_sampled(z, d, x, None, T, T, 1.0, 0.0, 9, 0)
+    assert list(out["status"]) == [0, S.ROW_NONFINITE, S.ROW_NONFINITE]
+    assert out["accepted"][0] == 0 and out["p_draft"][0, 0] < 1e-12
+    assert np.all(out["p_draft"][0, 1:] == -1) and np.all(out["p_draft"][1:] == -1)
