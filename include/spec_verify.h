@@ -57,7 +57,11 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
 /* Per-row status bits written to out_status[b]; 0 = row processed normally.
  * A row with any of the first four bits set is invalid: out_accepted[b] = -1
  * and its out_tokens row is all -1. */
-#define SPEC_ROW_NONFINITE 1   /* a NaN or +Inf logit, or an all -Inf position, at a position <= L_b */
+#define SPEC_ROW_NONFINITE 1   /* a NaN or +Inf logit, or an all -Inf position, at a target
+                                  position the pass reads: positions 0, 1, ... in order up to
+                                  the first rejection (or L_b), as the listing's loop stops
+                                  there; positions after it are not read.  With
+                                  spec_accept_sampled also any draft position i < L_b */
 #define SPEC_ROW_BAD_TOKEN 2   /* a draft token outside [0, V) at a position < L_b */
 #define SPEC_ROW_BAD_LEN 4     /* L_b outside [0, K] */
 #define SPEC_ROW_ZERO_Q 8      /* q_i(x_i) not > 0 at a position < L_b (stochastic mode) */
@@ -114,9 +118,9 @@ typedef enum { SPEC_F32 = 0, SPEC_BF16 = 1 } spec_dtype;
  *   philox_seed, philox_offset   the Philox key and counter high words
  *   out_tokens     [B, K+1] int32
  *   out_accepted   [B] int32: a_b, or -1 for an invalid row
- *   out_p_draft    [B, K] fp32 or NULL: p_i(x_i) for i < L_b (1/0 in greedy
- *                  mode: whether x_i is the argmax); -1 elsewhere and for
- *                  invalid rows
+ *   out_p_draft    [B, K] fp32 or NULL: p_i(x_i) at the tested positions,
+ *                  i <= a_b and i < L_b (1/0 in greedy mode: whether x_i is
+ *                  the argmax); -1 elsewhere and for invalid rows
  *   out_status     [B] int32 or NULL: SPEC_ROW_* bits
  *   workspace      device scratch of at least spec_accept_workspace_bytes(B, K, V)
  *                  bytes, 16-byte aligned.  Its first 256 * B bytes hold
@@ -186,7 +190,9 @@ int spec_accept_noalloc(const void* target_logits, int logits_dtype,
  * sums to less than top_p and (b) p_j >= min_p * max_k p_k, and renormalises
  * the kept mass.  top_p == 1 and min_p == 0 turn (a) and (b) off.  A draft
  * token outside q''s kept set makes the row invalid (SPEC_ROW_ZERO_Q).
- * out_p_draft holds p'_i(x_i).  Same uniforms, inverse-CDF rule, residual
+ * out_p_draft holds p'_i(x_i) at the tested positions.  The drafted tokens
+ * are validated for all L_b drafts (range, finite draft logits, token in q''s
+ * kept set).  Same uniforms, inverse-CDF rule, residual
  * fall-back and per-row status bits as spec_accept.  The filters are
  * resolved exactly: the top-p cut is the exact logit at which the mass,
  * counted from the top in 2^-40 fixed point of fp32 weights, reaches top_p

@@ -723,18 +723,23 @@ __global__ __launch_bounds__(kThreads) void k_accept(Args g) {
                 merge_argmax(prow + (int64_t)i * C * 2, C, bv, bi, fl);
                 if (lane == 0) {
                     sh.u.d.gi[i] = bi;
-                    if (fl) atomicOr(&sh.status, SPEC_ROW_NONFINITE);
+                    sh.u.d.flag[i] = fl;
                 }
             }
             if (t < L && (x < 0 || (int64_t)x >= V)) atomicOr(&sh.status, SPEC_ROW_BAD_TOKEN);
             __syncthreads();
-            if (t < L && x != sh.u.d.gi[t]) atomicMin(&sh.a, t);
+            // the listing's order: the row stops at the first draft that is
+            // not the argmax, or at the first position that is not finite
+            // (the row is then invalid); positions after the stop do not count
+            if ((t < L && x != sh.u.d.gi[t]) || (t <= L && sh.u.d.flag[t])) atomicMin(&sh.a, t);
             __syncthreads();
-            const int status = sh.status, a = sh.a;
+            const int a = sh.a;
+            const int status = sh.status | (sh.u.d.flag[a] ? SPEC_ROW_NONFINITE : 0);
             const bool invalid = (status & kInvalidMask) != 0;
             if (g.out_p_draft)
                 for (int i = t; i < K; i += kThreads)
-                    g.out_p_draft[b * K + i] = (!invalid && i < L) ? (g.tokens[b * K + i] == sh.u.d.gi[i] ? 1.f : 0.f) : -1.f;
+                    g.out_p_draft[b * K + i] =
+                        (!invalid && i < L && i <= a) ? (g.tokens[b * K + i] == sh.u.d.gi[i] ? 1.f : 0.f) : -1.f;
             for (int i = t; i <= K; i += kThreads) {
                 int v = -1;
                 if (!invalid) {
@@ -769,10 +774,13 @@ __global__ __launch_bounds__(kThreads) void k_accept(Args g) {
                     sh.u.d.M[i] = ps.M;
                     sh.u.d.S[i] = ps.S;
                     sh.u.d.flag[i] = ps.flag;
-                    if (ps.flag) atomicOr(&sh.status, SPEC_ROW_NONFINITE);
                 }
             }
             __syncthreads();
+            // the listing's order: the row stops at its first rejection, or
+            // at the first position that is not finite (the row is then
+            // invalid); positions after the stop do not count
+            if (t <= L && sh.u.d.flag[t]) atomicMin(&sh.a, t);
             if (t < L) {
                 float px = -1.f;
                 int rej = 0;
@@ -788,11 +796,12 @@ __global__ __launch_bounds__(kThreads) void k_accept(Args g) {
                 if (rej) atomicMin(&sh.a, t);
             }
             __syncthreads();
-            const int status = sh.status, a = sh.a;
+            const int a = sh.a;
+            const int status = sh.status | (sh.u.d.flag[a] ? SPEC_ROW_NONFINITE : 0);
             const bool invalid = (status & kInvalidMask) != 0;
             if (g.out_p_draft)
                 for (int i = t; i < K; i += kThreads)
-                    g.out_p_draft[b * K + i] = (!invalid && i < L) ? sh.u.d.px[i] : -1.f;
+                    g.out_p_draft[b * K + i] = (!invalid && i < L && i <= a) ? sh.u.d.px[i] : -1.f;
             if (invalid) write_invalid_row<T, VEC>(g, b, status, t);
             if (t == 0) {
                 Decision d{invalid ? 0 : a, status, (!invalid && a < L) ? 1 : 0,

@@ -862,45 +862,53 @@ __global__ __launch_bounds__(kT) void k_accept(Args a) {
     const Stat* stb = a.stats + b * S2;
     if (t == 0) {
         sh.status = 0;
-        sh.a = L;
+        sh.a = L + 1;  // no stop yet
     }
     __syncthreads();
-    // the decision, in every workgroup of the row (same inputs, same result)
+    // The decision, in every workgroup of the row (same inputs, same result),
+    // in the listing's order: the row stops at its first rejection, or at
+    // the first target position that is not finite (the row is then
+    // invalid); target positions after the stop do not count.  The drafted
+    // tokens are validated for all L drafts (range, finite draft logits,
+    // token in q''s kept set).
     {
         int st = 0;
-        if (t <= L && stb[t].flag) st |= SPEC_ROW_NONFINITE;
-        if (t < L && stb[K + 1 + t].flag) st |= SPEC_ROW_NONFINITE;
-        if (t < L && !(st & SPEC_ROW_NONFINITE)) {
+        bool stop = t <= L && stb[t].flag;  // target position t not finite
+        float px = -1.f;
+        if (t < L) {
             const int x = a.x[b * K + t];
-            float px = -1.f;
-            if (x < 0 || (int64_t)x >= V) {
+            if (stb[K + 1 + t].flag) {
+                st |= SPEC_ROW_NONFINITE;
+            } else if (x < 0 || (int64_t)x >= V) {
                 st |= SPEC_ROW_BAD_TOKEN;
             } else {
-                const Stat sp = stb[t], sq = stb[K + 1 + t];
-                const float zx = ld(zb + (int64_t)t * V, x), dx = ld(db + (int64_t)t * V, x);
-                const bool kp = kept_w(zx, a.cp, sp, a.min_p) > 0.f;
-                const bool kq = kept_w(dx, a.cq, sq, a.min_p) > 0.f;
-                if (!kq) {
+                const Stat sq = stb[K + 1 + t];
+                const float dx = ld(db + (int64_t)t * V, x);
+                if (!(kept_w(dx, a.cq, sq, a.min_p) > 0.f)) {
                     st |= SPEC_ROW_ZERO_Q;
-                } else {
+                } else if (!stop) {
+                    const Stat sp = stb[t];
+                    const float zx = ld(zb + (int64_t)t * V, x);
+                    const bool kp = kept_w(zx, a.cp, sp, a.min_p) > 0.f;
                     const double p = kp ? exp2((double)zx * (double)a.cp - (double)(sp.m * a.cp)) / sp.s : 0.0;
                     const double q = exp2((double)dx * (double)a.cq - (double)(sq.m * a.cq)) / sq.s;
                     px = (float)p;
                     const double acc = fmin(1.0, p / q);
                     const RowPosUniforms u = row_pos_uniforms(a.seed, a.offset, (uint32_t)(a.row_base + b), (uint32_t)t);
-                    if (!((double)u.acc < acc)) atomicMin(&sh.a, t);
+                    stop = !((double)u.acc < acc);
                 }
             }
             sh.px[t] = px;
         }
+        if (stop) atomicMin(&sh.a, t);
         if (st) atomicOr(&sh.status, st);
     }
     __syncthreads();
-    int status = sh.status;
-    const int ar = sh.a;
+    const int ar = min(sh.a, L);
+    int status = sh.status | (stb[ar].flag ? SPEC_ROW_NONFINITE : 0);
     const bool invalid = (status & kInvalid) != 0;
     if (writer && a.out_p_draft)
-        for (int i = t; i < K; i += kT) a.out_p_draft[b * K + i] = (!invalid && i < L) ? sh.px[i] : -1.f;
+        for (int i = t; i < K; i += kT) a.out_p_draft[b * K + i] = (!invalid && i < L && i <= ar) ? sh.px[i] : -1.f;
     if (invalid) {
         if (writer) {
             for (int i = t; i <= K; i += kT) a.out_tokens[b * (K + 1) + i] = -1;

@@ -157,9 +157,12 @@ def test_status_bits_match_oracle():
     inp = workloads.accept_inputs(10, 3, 9000, logit_std=2.0, draft_noise=1.0, temperature=1.0,
                                   seed=9)
     z = inp.logits.float().numpy().copy()
-    z[0, 1, 17] = np.nan
-    z[1, 3, 8500] = np.inf
-    z[2, 2, :] = -np.inf
+    # position 0 is always read: these rows are invalid whatever is drawn
+    z[0, 0, 17] = np.nan
+    z[1, 0, 8500] = np.inf
+    z[2, 0, :] = -np.inf
+    # read only if the drafts before it are accepted: GPU and oracle agree
+    z[9, 2, 123] = np.nan
     z[3, 0, :100] = -np.inf          # partial -inf: valid
     z[4, 0, 8192:] = -np.inf         # a whole -inf chunk: valid
     z[5, 3, 4000] = np.nan           # past L_b below: not read
@@ -237,9 +240,9 @@ def test_draft_equal_to_target():
 def test_give_up_path_leaves_the_workspace_valid():
     # A wait bound of one poll makes most workgroups give up on their row's
     # decision (every kernel still ends normally).  Stalled rows report
-    # ROW_STALLED with -1 outputs, every other row matches the oracle, the
-    # row records are zero afterwards, and the next call on the same
-    # workspace is exact again.
+    # ROW_STALLED with -1 outputs and every other row matches the oracle.
+    # The workspace stays valid: the next call on it (default bound) is
+    # exact and byte-identical to a call on a freshly zeroed workspace.
     inp = workloads.accept_inputs(48, 5, 60000, logit_std=3.0, draft_noise=1.0, temperature=0.8,
                                   seed=44, bf16=True, ragged=True)
     z, q = inp.logits.cuda(), _dev(inp.draft_probs)
@@ -253,7 +256,6 @@ def test_give_up_path_leaves_the_workspace_valid():
                                      workspace=ws))
     finally:
         sv.set_wait_bound(0)
-    assert torch.count_nonzero(ws[:256 * B]).item() == 0, "row records not reset"
     o = oracle.spec_accept(inp.logits_f32(), inp.draft_probs, inp.draft_tokens, inp.draft_lens,
                            0.8, inp.seed, 3, nthreads=NTHREADS)
     stalled = got["status"] == sv.ROW_STALLED
@@ -264,9 +266,13 @@ def test_give_up_path_leaves_the_workspace_valid():
     sub = {k: v[keep] for k, v in got.items()}
     osub = {k: v[keep] for k, v in o.items()}
     compare(sub, osub, K, label="rows that did not stall")
-    # the same workspace, default bound: every row exact
-    print("[spec_accept] give-up path: default bound on the same workspace", flush=True)
-    g2 = gpu_to_numpy(sv.accept(z, q, x, L, temperature=0.8, seed=inp.seed, offset=3, workspace=ws))
-    assert not np.any(g2["status"] == sv.ROW_STALLED)
-    compare(g2, o, K, label="after a stalled call")
-    assert torch.count_nonzero(ws[:256 * B]).item() == 0
+    # the same workspace, default bound: every row exact, twice in a row
+    for rep in range(2):
+        print(f"[spec_accept] give-up path: default bound on the same workspace ({rep})", flush=True)
+        g2 = gpu_to_numpy(sv.accept(z, q, x, L, temperature=0.8, seed=inp.seed, offset=3,
+                                    workspace=ws))
+        assert not np.any(g2["status"] == sv.ROW_STALLED)
+        compare(g2, o, K, label="after a stalled call")
+    fresh = gpu_to_numpy(sv.accept(z, q, x, L, temperature=0.8, seed=inp.seed, offset=3))
+    for k in fresh:
+        assert np.array_equal(fresh[k], g2[k]), k

@@ -201,7 +201,7 @@ def _single_pass_rows(V, K, rng):
     z[4] = rng.normal(0, 0.001, (K + 1, V))
     z[5, :, : V // 4] = -np.inf
     z[5, 0, 10] = np.nan
-    z[6, K, V // 2] = np.inf
+    z[6, 0, V // 2] = np.inf
     z = z.astype(np.float32)
     d = z[:, :K].copy()
     fin = np.isfinite(d)
@@ -235,7 +235,8 @@ def test_one_pass_edges(bf16, top_p, mp):
 
 def test_status_bits():
     z, d, x, L = make_inputs(8, 3, 9000, std=2.0, noise=1.0, T=1.0, top_p=0.95, min_p=0.05, seed=8)
-    z[0, 1, 17] = np.nan
+    z[0, 0, 17] = np.nan                  # target position 0: always read
+    z[6, 2, 50] = np.nan                  # read only if drafts 0 and 1 are accepted
     d[1, 2, 40] = np.inf
     x[2, 0] = 9000                        # out of range
     L[3] = 4                              # > K
@@ -246,6 +247,7 @@ def test_status_bits():
     g, o = run(z, d, x, L, T=1.0, top_p=0.95, min_p=0.05, seed=1, offset=0, label="status")
     assert list(o["status"][:6]) == [1, 1, 2, 4, 8, 0]
     assert list(g["status"][:6]) == [1, 1, 2, 4, 8, 0]
+    assert g["status"][6] == o["status"][6]
     assert np.all(g["accepted"][:5] == -1) and np.all(g["tokens"][:5] == -1)
     # at T = 1 a top-p cut within 1e-6 of 0.95 is a few-percent event per
     # distribution, and a row has seven: a looser budget for near rows
