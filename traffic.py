@@ -148,6 +148,28 @@ def markdown(res, command):
     return "\n".join(lines) + "\n"
 
 
+def kernel_stats(trace_csv, top=24):
+    """Markdown table of kernel durations from a rocprofv3 --kernel-trace CSV,
+    one row per (kernel, grid size): the library's kernels split by launch
+    shape (the lm-head product runs as whole tiles, then a K-split tail)."""
+    groups = {}
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            key = (_short(r["Kernel_Name"]), grid if "specv" in r["Kernel_Name"] else None)
+            d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+            groups.setdefault(key, []).append(d)
+    total = sum(sum(v) for v in groups.values())
+    lines = ["| kernel | grid (threads) | calls | avg us | median us | min us | max us | % of GPU time |",
+             "|---|---|---|---|---|---|---|---|"]
+    for (name, grid), ds in sorted(groups.items(), key=lambda kv: -sum(kv[1]))[:top]:
+        ds = sorted(ds)
+        lines.append(f"| `{name[:90]}` | {grid if grid is not None else '-'} | {len(ds)} | "
+                     f"{sum(ds) / len(ds):.2f} | {ds[len(ds) // 2]:.2f} | {ds[0]:.2f} | {ds[-1]:.2f} | "
+                     f"{100 * sum(ds) / total:.2f} |")
+    return "\n".join(lines) + "\n"
+
+
 def read_committed(path):
     """The traffic figures of a committed summary if they describe the current
     sources, else None."""
@@ -170,9 +192,14 @@ def main(argv=None):
     ap.add_argument("--summarize", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the markdown summary of two counter runs to stdout")
     ap.add_argument("--command", default="", help="the profiling commands, quoted in the summary")
+    ap.add_argument("--kernel-stats", metavar="TRACE_CSV",
+                    help="print a table of kernel durations from a --kernel-trace CSV")
     args = ap.parse_args(argv)
     if args.digest:
         print(source_digest())
+        return
+    if args.kernel_stats:
+        print(kernel_stats(args.kernel_stats), end="")
         return
     if args.summarize:
         print(markdown(summarize(*args.summarize), args.command), end="")
