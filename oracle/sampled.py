@@ -119,6 +119,105 @@ def _inv_cdf(w, u):
     return j, near
 
 
+def _filter_parts(z, T: float, top_p: float, min_p: float):
+    """The pieces of one position's filtered distribution: (p fp64 [V], the
+    top-p keep test [V], the min-p keep test [V], the ambiguous decisions),
+    or None for a non-finite position.  An ambiguous decision is one value's
+    keep test (criterion 0: top-p, its mass-above against top_p; 1: min-p,
+    p_j / max p against min_p) that lies within 1e-6 of its threshold, with
+    the mask of the tokens holding that value."""
+    z64 = np.asarray(z, dtype=np.float64)
+    if not np.all(np.isfinite(z64) | (z64 == -np.inf)) or np.all(z64 == -np.inf):
+        return None
+    m = z64.max()
+    e = np.exp((z64 - m) / T)
+    p = e / e.sum()
+    top = np.ones(z64.shape[0], bool)
+    mn = np.ones(z64.shape[0], bool)
+    amb = []
+    if top_p < 1.0:
+        vals, inv = np.unique(z64, return_inverse=True)
+        mass = np.bincount(inv, weights=p, minlength=vals.shape[0])
+        above = np.cumsum(mass[::-1])[::-1] - mass
+        top = (above < top_p)[inv]
+        for k in np.nonzero(np.abs(above - top_p) < NEAR)[0]:
+            amb.append((0, inv == k))
+    if min_p > 0.0:
+        mn = e >= min_p
+        for v in np.unique(z64[np.abs(e - min_p) < NEAR * min_p]):
+            amb.append((1, z64 == v))
+    return p, top, mn, amb
+
+
+def _renorm(parts, flips=()):
+    """p' of a position with the ambiguous decisions `flips` (indices into
+    its ambiguous list) taken the other way; None if nothing stays kept.
+    With no flips this is filtered()'s p', the same operations."""
+    p, top, mn, amb = parts
+    if flips:
+        top, mn = top.copy(), mn.copy()
+        for k in flips:
+            crit, mask = amb[k]
+            if crit == 0:
+                top[mask] = ~top[mask]
+            else:
+                mn[mask] = ~mn[mask]
+    keep = top & mn
+    pk = np.where(keep, p, 0.0)
+    tot = pk.sum()
+    return pk / tot if tot > 0.0 else None
+
+
+def _row_outcome(L, K, V, xb, qd, pd, seed, offset, gr):
+    """One row of the pass given q'_i (i < L) and p'_i (i <= L) (None: not
+    finite).  Returns (status, a_b, tokens tuple, p_draft [K], near), near
+    when the acceptance test or the draw lies within 1e-6 of its threshold;
+    a_b = -1 and tokens None for an invalid row."""
+    # the drafted tokens are validated for all L drafts: each draft
+    # distribution q'_i, the token's range, and the token in q''s kept set
+    st = 0
+    for i in range(L):
+        if qd[i] is None:
+            st |= ROW_NONFINITE
+        if not 0 <= xb[i] < V:
+            st |= ROW_BAD_TOKEN
+        elif qd[i] is not None and not qd[i][xb[i]] > 0.0:
+            st |= ROW_ZERO_Q
+    pdraft = np.full(K, -1.0)
+    if st:
+        return st, -1, None, pdraft, False
+    # the target's distributions in the listing's order: position i only
+    # when every draft before it was accepted, the bonus position L only when
+    # all were; a non-finite position read this way makes the row invalid
+    a, near = L, False
+    for i in range(L + 1):
+        if pd[i] is None:
+            return ROW_NONFINITE, -1, None, np.full(K, -1.0), near
+        if i == L:
+            break
+        px, qx = pd[i][xb[i]], qd[i][xb[i]]
+        pdraft[i] = px
+        acc = min(1.0, px / qx)
+        ua, _ = _orc.uniforms(seed, offset, gr, i)
+        near |= abs(ua - acc) < NEAR
+        if not ua < acc:
+            a = i
+            break
+    _, us = _orc.uniforms(seed, offset, gr, a)
+    if a < L:
+        w = np.maximum(pd[a] - qd[a], 0.0)
+        if not w.sum() > 0.0:
+            w = pd[a]
+            st |= ROW_RESID_ZERO
+    else:
+        w = pd[L]
+    tok, nr = _inv_cdf(w, us)
+    return st, a, tuple(int(v) for v in xb[:a]) + (tok,), pdraft, near | nr
+
+
+MAX_AMBIGUOUS = 4  # ambiguous filter decisions per row enumerated; more: the row is near
+
+
 def spec_accept_sampled(target_logits, draft_logits, draft_tokens, draft_lens, T_target: float,
                         T_draft: float, top_p: float, min_p: float, seed: int, offset: int,
                         row_base: int = 0) -> dict:
@@ -127,10 +226,15 @@ def spec_accept_sampled(target_logits, draft_logits, draft_tokens, draft_lens, T
     Temperatures, top_p and min_p are rounded to fp32 as the GPU receives
     them.  Returns tokens [B, K+1] (-1 padded), accepted [B] (-1 invalid),
     p_draft [B, K] (p'_i(x_i) at the tested positions, -1 elsewhere), status
-    [B], near [B] (a decision the row's outcome depends on lay within 1e-6
-    of its threshold: a filter cut at a target position read or a draft
-    position tested, the kept-set test of a draft token, an acceptance test
-    or the draw)."""
+    [B], near [B] and p_draft_lo / p_draft_hi [B, K].
+
+    near: the row's outcome (status, a_b, tokens) is not pinned to 1e-6 --
+    its acceptance test or draw lies within 1e-6 of its threshold, or taking
+    any of its ambiguous filter decisions (a keep test within 1e-6 of its
+    threshold, in any of the row's distributions) the other way changes the
+    outcome, or it has more than MAX_AMBIGUOUS of them.  Every combination
+    of the ambiguous decisions is tried.  p_draft_lo / hi bound p'_i(x_i)
+    over those combinations (equal to p_draft when none is ambiguous)."""
     z = np.asarray(target_logits, dtype=np.float32)
     d = np.asarray(draft_logits, dtype=np.float32)
     B, K1, V = z.shape
@@ -141,79 +245,50 @@ def spec_accept_sampled(target_logits, draft_logits, draft_tokens, draft_lens, T
     tp, mp = float(np.float32(top_p)), float(np.float32(min_p))
     out = dict(tokens=np.full((B, K1), -1, np.int32), accepted=np.full(B, -1, np.int32),
                p_draft=np.full((B, K), -1.0), status=np.zeros(B, np.int32),
-               near=np.zeros(B, bool))
+               near=np.zeros(B, bool), p_draft_lo=np.full((B, K), -1.0),
+               p_draft_hi=np.full((B, K), -1.0))
     for b in range(B):
         L = int(Ls[b])
         if L < 0 or L > K:
             out["status"][b] = ROW_BAD_LEN
             continue
-        # the drafted tokens are validated for all L drafts: each draft
-        # distribution q'_i, the token's range, and the token in q''s kept set
-        st = 0
-        qs, qnear = [], []
-        for i in range(L):
-            qf, _, nr, bad = filtered(d[b, i], Tq, tp, mp)
-            st |= ROW_NONFINITE if bad else 0
-            qs.append(qf)
-            qnear.append(nr)
-        ztok = []   # whether the kept-set test of x_i lies near a filter cut
-        for i in range(L):
-            if not 0 <= x[b, i] < V:
-                st |= ROW_BAD_TOKEN
-            elif qs[i] is not None:
-                ztok.append(bool(near_tokens(d[b, i], Tq, tp, mp)[x[b, i]]))
-                if not qs[i][x[b, i]] > 0.0:
-                    st |= ROW_ZERO_Q
-        if st:
-            out["status"][b] = st
-            out["near"][b] = any(ztok)
-            continue
-        # the target's distributions in the listing's order: position i only
-        # when every draft before it was accepted, position L (the bonus) only
-        # when all were; a non-finite position read this way makes the row
-        # invalid, positions after the stop are never read
         gr = row_base + b
-        a, nearrow, ps, bad = L, False, {}, False
-        for i in range(L + 1):
-            pf, _, nr, badp = filtered(z[b, i], Tp, tp, mp)
-            if badp:
-                bad = True
-                break
-            ps[i] = pf
-            nearrow |= nr
-            if i == L:
-                break
-            nearrow |= qnear[i]
-            px, qx = pf[x[b, i]], qs[i][x[b, i]]
-            out["p_draft"][b, i] = px
-            acc = min(1.0, px / qx)
-            ua, _ = _orc.uniforms(seed, offset, gr, i)
-            nearrow |= abs(ua - acc) < NEAR
-            if not ua < acc:
-                a = i
-                break
-        # drafts past the stop matter only through their kept-set test
-        nearrow |= any(ztok[a + 1:]) if not bad else any(ztok[i + 1:])
-        if bad:
-            out["p_draft"][b] = -1.0
-            out["status"][b] = ROW_NONFINITE
-            out["near"][b] = nearrow
-            continue
-        _, us = _orc.uniforms(seed, offset, gr, a)
-        if a < L:
-            w = np.maximum(ps[a] - qs[a], 0.0)
-            if not w.sum() > 0.0:
-                w = ps[a]
-                st |= ROW_RESID_ZERO
+        qparts = [_filter_parts(d[b, i], Tq, tp, mp) for i in range(L)]
+        pparts = [_filter_parts(z[b, i], Tp, tp, mp) for i in range(L + 1)]
+        dists = qparts + pparts   # q'_0 .. q'_{L-1}, then p'_0 .. p'_L
+        amb = [(k, j) for k, pa in enumerate(dists) if pa is not None for j in range(len(pa[3]))]
+        nominal = [None if pa is None else _renorm(pa) for pa in dists]
+        st, a, toks, pdraft, near = _row_outcome(L, K, V, x[b], nominal[:L], nominal[L:], seed, offset, gr)
+        lo, hi = pdraft.copy(), pdraft.copy()
+        if len(amb) > MAX_AMBIGUOUS:
+            near = True
         else:
-            w = ps[L]
-        tok, nr = _inv_cdf(w, us)
-        nearrow |= nr
-        out["tokens"][b, :a] = x[b, :a]
-        out["tokens"][b, a] = tok
-        out["accepted"][b] = a
+            for combo in range(1, 1 << len(amb)):
+                flips = {}
+                for bit, (k, j) in enumerate(amb):
+                    if combo >> bit & 1:
+                        flips.setdefault(k, []).append(j)
+                alt = list(nominal)
+                for k, js in flips.items():
+                    alt[k] = _renorm(dists[k], tuple(js))
+                if any(alt[k] is None for k in flips):
+                    near = True
+                    continue
+                st2, a2, toks2, pd2, _ = _row_outcome(L, K, V, x[b], alt[:L], alt[L:], seed, offset, gr)
+                if (st2, a2, toks2) != (st, a, toks):
+                    near = True
+                else:
+                    t_ = pd2 >= 0
+                    lo[t_] = np.minimum(lo[t_], pd2[t_])
+                    hi[t_] = np.maximum(hi[t_], pd2[t_])
         out["status"][b] = st
-        out["near"][b] = nearrow
+        out["near"][b] = near
+        out["p_draft"][b] = pdraft
+        out["p_draft_lo"][b] = lo
+        out["p_draft_hi"][b] = hi
+        if toks is not None:
+            out["accepted"][b] = a
+            out["tokens"][b, :a + 1] = toks
     return out
 
 

@@ -76,9 +76,12 @@ def compare(g, o, label, max_near=0.05):
     assert np.array_equal(st_g[ok], o["status"][ok]), (label, np.nonzero(st_g[ok] != o["status"][ok]))
     assert np.array_equal(g["accepted"][ok], o["accepted"][ok]), label
     assert np.array_equal(g["tokens"][ok], o["tokens"][ok]), label
+    # p'(x) within 1e-5 of the oracle's, or of the range it spans when a
+    # filter decision is ambiguous without changing the outcome
     m = ok[:, None] & (o["p_draft"] >= 0)
-    pg, po = g["p_draft"][m].astype(np.float64), o["p_draft"][m]
-    assert np.all(np.abs(pg - po) <= 1e-5 * np.maximum(po, 1e-30) + 1e-12), label
+    pg = g["p_draft"][m].astype(np.float64)
+    lo, hi = o["p_draft_lo"][m], o["p_draft_hi"][m]
+    assert np.all((pg >= lo * (1 - 1e-5) - 1e-12) & (pg <= hi * (1 + 1e-5) + 1e-12)), label
     assert np.all(g["p_draft"][~(o["p_draft"] >= 0) & ok[:, None]] == -1.0)
     return dict(rows=len(ok), near=int(near.sum()), accepted_mean=float(o["accepted"][ok].mean()))
 
@@ -122,12 +125,14 @@ def test_bench_size_sampled_rows():
     g = {k: getattr(res, k).cpu().numpy() for k in ("tokens", "accepted", "p_draft", "status")}
     zh, dh = z.float().cpu().numpy(), d.float().cpu().numpy()
     xh, Lh = x.cpu().numpy(), L.cpu().numpy()
-    rows = sorted({0, B - 1, *np.random.default_rng(7).integers(0, B, 8).tolist()})
+    rows = sorted({0, B - 1, *np.random.default_rng(7).integers(0, B, 16).tolist()})
     gs = {k: v[rows] for k, v in g.items()}
     parts = [S.spec_accept_sampled(zh[b:b + 1], dh[b:b + 1], xh[b:b + 1], Lh[b:b + 1], 0.8, 0.8, 0.95, 0.05, 77, 0,
                                    row_base=b) for b in rows]
     o = {k: np.concatenate([p_[k] for p_ in parts]) for k in parts[0]}
-    print(compare(gs, o, "bench size", max_near=0.5))
+    st = compare(gs, o, "bench size", max_near=0.1)
+    print(st)
+    assert st["rows"] >= 12
 
 
 @pytest.mark.parametrize("bf16", [False, True])
@@ -152,19 +157,20 @@ def test_top_p_alone_peaked(bf16):
             x[b, i] = rng.choice(V, p=q / q.sum())
     g, o = run(z, d, x, rng.integers(0, K + 1, B).astype(np.int32), T=T, top_p=tp, min_p=0.0, seed=8, offset=2,
                bf16=bf16, label="top-p alone, peaked")
-    print(compare(g, o, ("top-p alone", bf16), max_near=0.5))
+    print(compare(g, o, ("top-p alone", bf16), max_near=0.13))
 
 
 def test_flat_distribution_deep_top_p_cut():
     # small logit spread: the top-p cut falls deep in the vocabulary, in a
     # crossing bin with many entries.  Distinct logits then sit ~3e-5 of mass
     # apart, so a cut within the 1e-6 window of top_p is not rare (~7% per
-    # distribution): more rows, a looser budget for near-threshold rows.
+    # distribution); a row is excluded only when taking such a cut the other
+    # way changes its outcome.
     z, d, x, L = make_inputs(16, 3, 30000, std=0.3, noise=0.1, T=1.0, top_p=0.9, min_p=0.0, seed=6)
     g, o = run(z, d, x, L, T=1.0, top_p=0.9, min_p=0.0, seed=3, offset=0, label="flat")
-    st = compare(g, o, "flat", max_near=0.6)
+    st = compare(g, o, "flat", max_near=0.13)
     print(st)
-    assert st["rows"] - st["near"] >= 6
+    assert st["rows"] - st["near"] >= 14
 
 
 def test_different_draft_temperature_and_edges():
@@ -180,7 +186,7 @@ def test_different_draft_temperature_and_edges():
                 x[b, i] = rng.choice(V, p=q / q.sum())
         g, o = run(z, d, x, L, T=0.7, Td=1.3, top_p=0.9, min_p=0.05, seed=2, offset=5, bf16=bf16,
                    label=f"edge {B},{K},{V}")
-        compare(g, o, ("edge", B, K, V), max_near=0.5)
+        print(compare(g, o, ("edge", B, K, V), max_near=0.34))
 
 
 def _single_pass_rows(V, K, rng):
@@ -230,7 +236,7 @@ def test_one_pass_edges(bf16, top_p, mp):
     assert o["status"][5] == S.ROW_NONFINITE and o["status"][6] == S.ROW_NONFINITE
     assert (g["status"][5] & S.ROW_NONFINITE) and (g["status"][6] & S.ROW_NONFINITE)
     assert not np.any(o["status"][[0, 1, 2, 3, 4, 7]])
-    compare(g, o, ("one-pass edges", bf16, top_p, mp), max_near=0.5)
+    print(compare(g, o, ("one-pass edges", bf16, top_p, mp), max_near=0.13))
 
 
 def test_status_bits():
@@ -250,8 +256,8 @@ def test_status_bits():
     assert g["status"][6] == o["status"][6]
     assert np.all(g["accepted"][:5] == -1) and np.all(g["tokens"][:5] == -1)
     # at T = 1 a top-p cut within 1e-6 of 0.95 is a few-percent event per
-    # distribution, and a row has seven: a looser budget for near rows
-    compare(g, o, "status", max_near=0.5)
+    # distribution; a row is excluded only when it decides the outcome
+    print(compare(g, o, "status", max_near=0.13))
 
 
 def test_tiny_vocab_distribution_and_parity():

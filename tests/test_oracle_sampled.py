@@ -159,3 +159,60 @@ def test_positions_after_the_first_rejection_are_not_read():
     assert list(out["status"]) == [0, S.ROW_NONFINITE, S.ROW_NONFINITE]
     assert out["accepted"][0] == 0 and out["p_draft"][0, 0] < 1e-12
     assert np.all(out["p_draft"][0, 1:] == -1) and np.all(out["p_draft"][1:] == -1)
+
+
+def _ambiguous_case():
+    """V = 16, T = 1: p at position 0 = [0.5, 0.3, 0.15, 0.05/13 ...], so the
+    mass above token 2 is 0.8 = top_p up to fp32 rounding of the logits (its
+    top-p test is ambiguous); q = [0.6, 0.35/14 ..., 0.05 at token 2, ...]
+    keeps every token firmly.  Position 1 is unambiguous (flat)."""
+    V = 16
+    p0 = np.full(V, 0.05 / 13)
+    p0[:3] = [0.5, 0.3, 0.15]
+    q0 = np.full(V, 0.35 / 14)
+    q0[0], q0[2] = 0.6, 0.05
+    z = np.zeros((1, 2, V), np.float32)
+    z[0, 0] = np.log(p0)
+    d = np.log(q0).astype(np.float32)[None, None, :]
+    return z, d, float(np.float32(0.8))
+
+
+def test_near_when_an_ambiguous_cut_decides_the_row():
+    # x = token 2: kept, p'(2) = 0.15 / 0.95 > q'(2) = 0.05 and the draft is
+    # accepted whatever u; dropped, p'(2) = 0 and it is rejected.  The
+    # outcome hangs on the ambiguous cut, so the row is near.
+    z, d, tp = _ambiguous_case()
+    parts = S._filter_parts(z[0, 0], 1.0, tp, 0.0)
+    assert len(parts[3]) == 1 and parts[3][0][0] == 0 and parts[3][0][1][2]
+    o = S.spec_accept_sampled(z, d, np.array([[2]]), np.array([1]), 1.0, 1.0, tp, 0.0, 5, 0)
+    assert o["near"][0]
+
+
+def test_not_near_when_the_ambiguous_cut_does_not_matter():
+    # x = token 0: p'(0) = 0.5 / 0.95 or 0.5 / 0.8, q'(0) = 0.6, so the
+    # acceptance probability is 0.877 or 1; with u_acc below 0.8 the draft is
+    # accepted either way and the bonus draw at the flat position 1 is
+    # unambiguous: the row is pinned, and p'(0) is bounded by both values.
+    z, d, tp = _ambiguous_case()
+    off = next(o for o in range(200) if oracle.uniforms(5, o, 0, 0)[0] < 0.8)
+    o = S.spec_accept_sampled(z, d, np.array([[0]]), np.array([1]), 1.0, 1.0, tp, 0.0, 5, off)
+    assert not o["near"][0] and o["accepted"][0] == 1 and o["status"][0] == 0
+    lo, hi, pd = o["p_draft_lo"][0, 0], o["p_draft_hi"][0, 0], o["p_draft"][0, 0]
+    assert np.isclose(lo, 0.5 / 0.95, rtol=1e-6) and np.isclose(hi, 0.5 / 0.8, rtol=1e-6)
+    assert lo <= pd <= hi
+    # the earlier, coarser flag (any cut within 1e-6 at a position read) would
+    # have excluded this row
+    assert S.filtered(z[0, 0], 1.0, tp, 0.0)[2]
+
+
+def test_near_when_an_ambiguous_min_p_test_decides_the_kept_set():
+    # min-p at exactly p_2 / max p: token 2's min-p test is ambiguous; with
+    # x = 2 in the draft the row's validity (ZERO_Q) hangs on it
+    V = 8
+    q0 = np.full(V, 0.3 / 6)
+    q0[0], q0[2] = 0.6, 0.1
+    d = np.log(q0).astype(np.float32)[None, None, :]
+    z = np.zeros((1, 2, V), np.float32)
+    mp = float(np.float32(np.exp(float(d[0, 0, 2]) - float(d[0, 0, 0]))))
+    o = S.spec_accept_sampled(z, d, np.array([[2]]), np.array([1]), 1.0, 1.0, 1.0, mp, 5, 0)
+    assert o["near"][0]
