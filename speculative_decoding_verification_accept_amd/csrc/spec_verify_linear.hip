@@ -26,6 +26,10 @@
 //    straight into an LDS ring of 4-5 stages by loads that write LDS, so the
 //    prefetch distance costs no registers; W stays [k][n] in LDS and the
 //    transposing LDS read ds_read_b64_tr_b16 builds its MFMA operands.
+//    With 129-192 rows and at least 512 columns per compute unit (the
+//    lm-head), whole rounds of 192 x 512 tiles (16 waves, a 3-stage ring:
+//    half the X bytes per W byte of 192 x 256, 6% faster on the lm-head),
+//    then the remaining columns as 192 x 256 tiles.
 //  k_tile (other K): the earlier design, W staged through registers and
 //    transposed with v_perm_b32 on its way into LDS.
 // Split-K (when the tiles alone fill less than half the machine) writes fp32
@@ -787,10 +791,11 @@ using TileL = TileCfg<192, 256, 64, 96, 64>;
 using TileB = TileCfg<256, 128, 64, 64, 64>;
 using DmaS = DmaCfg<128, 128, 64, 2, 4, 4>;   // M in (16, 128], or (128, 256] on narrow N
 using DmaL = DmaCfg<192, 256, 32, 2, 4, 5>;   // M in (128, 192] on a wide N (lm-head)
+using DmaW = DmaCfg<192, 512, 32, 2, 8, 3>;   // M in (128, 192], N >= 512 columns per compute unit
 using DmaB = DmaCfg<256, 128, 32, 4, 2, 5>;   // M in (256, 512]
 using DmaH = DmaCfg<256, 256, 64, 2, 4, 2>;   // M > 512, K a multiple of 64
 
-enum Kern { kStrip1, kStrip2, kTileS, kTileL, kTileB, kDmaS, kDmaL, kDmaB, kDmaH };
+enum Kern { kStrip1, kStrip2, kTileS, kTileL, kTileB, kDmaS, kDmaL, kDmaB, kDmaH, kDmaWL };
 
 // One or two launches over ranges of n-tiles; each may split K.
 struct Launch {
@@ -821,6 +826,30 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
         return p;
     };
     if (M <= 16 || (M <= 32 && K % 64 != 0)) return strip_plan();
+    // the lm-head class (128 < M <= 192, at least one 192 x 512 tile per
+    // compute unit): whole rounds of 192 x 512 tiles, then the remaining
+    // columns as 192 x 256 tiles, split along K when they fill at most half
+    // the machine
+    if (M > 128 && M <= 192 && K % 32 == 0 && N / DmaW::BN >= cus) {
+        const int64_t nst = K / DmaL::BK;
+        p.kern = kDmaWL;
+        p.mtiles = 1;
+        const int64_t tw = N / DmaW::BN / cus * cus;  // 512-column tiles in whole rounds
+        const int64_t c0 = tw * DmaW::BN;
+        p.l[0] = Launch{0, tw, 1};
+        p.nl = 1;
+        p.ntiles = tw;
+        if (c0 < N) {
+            const int64_t t0 = c0 / DmaL::BN, t1 = (N + DmaL::BN - 1) / DmaL::BN, rem = t1 - t0;
+            int s2 = 1;
+            if (2 * rem <= cus && nst >= 16) s2 = (int)(cus / rem) > 4 ? 4 : (int)(cus / rem);
+            p.l[1] = Launch{t0, t1, s2};
+            p.nl = 2;
+            p.ntiles = t1;
+            if (s2 > 1) p.ws_bytes = align_up((size_t)s2 * M * rem * DmaL::BN * sizeof(float), 256);
+        }
+        return p;
+    }
     int BM, BN, BK;
     auto pick = [&](Kern k, int bm, int bn, int bk) { p.kern = k; BM = bm; BN = bn; BK = bk; };
     if (K % 64 == 0 && M <= 128) {
@@ -919,16 +948,22 @@ int launch_tile(const Plan& p, const uint16_t* x, const uint16_t* w, void* Y, in
     return launch_reduce(l, Cfg::BN, N, partial, Y, yb, M, N, s);  // k_tile partials: row stride N
 }
 
+// One launch of k_dma<Cfg> over the n-tiles of l (and its split-K reduce).
+template <typename Cfg>
+int launch_dma_one(const Plan& p, const Launch& l, const uint16_t* x, const uint16_t* w, void* Y, int yb,
+                   int64_t M, int64_t N, int64_t K, float* partial, hipStream_t s) {
+    const int64_t NP = (l.t1 - l.t0) * Cfg::BN;
+    hipLaunchKernelGGL((k_dma<Cfg>), dim3((unsigned)p.mtiles, (unsigned)(l.t1 - l.t0), (unsigned)l.splits),
+                       dim3(Cfg::NT), 0, s, x, w, Y, yb, M, N, K, l.splits, partial, l.t0, NP);
+    if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
+    return launch_reduce(l, Cfg::BN, NP, partial, Y, yb, M, N, s);
+}
+
 template <typename Cfg>
 int launch_dma(const Plan& p, const uint16_t* x, const uint16_t* w, void* Y, int yb, int64_t M, int64_t N,
                int64_t K, float* partial, hipStream_t s) {
     for (int i = 0; i < p.nl; ++i) {
-        const Launch& l = p.l[i];
-        const int64_t NP = (l.t1 - l.t0) * Cfg::BN;
-        hipLaunchKernelGGL((k_dma<Cfg>), dim3((unsigned)p.mtiles, (unsigned)(l.t1 - l.t0), (unsigned)l.splits),
-                           dim3(Cfg::NT), 0, s, x, w, Y, yb, M, N, K, l.splits, partial, l.t0, NP);
-        if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
-        const int rc = launch_reduce(l, Cfg::BN, NP, partial, Y, yb, M, N, s);
+        const int rc = launch_dma_one<Cfg>(p, p.l[i], x, w, Y, yb, M, N, K, partial, s);
         if (rc != SPEC_OK) return rc;
     }
     return SPEC_OK;
@@ -974,6 +1009,11 @@ extern "C" int spec_verify_linear(const void* X, const void* W, void* Y, int y_d
         case kDmaL: return launch_dma<DmaL>(p, x, w, Y, yb, M, N, Kd, partial, s);
         case kDmaB: return launch_dma<DmaB>(p, x, w, Y, yb, M, N, Kd, partial, s);
         case kDmaH: return launch_dma<DmaH>(p, x, w, Y, yb, M, N, Kd, partial, s);
+        case kDmaWL: {
+            const int rc = launch_dma_one<DmaW>(p, p.l[0], x, w, Y, yb, M, N, Kd, partial, s);
+            if (rc != SPEC_OK || p.nl < 2) return rc;
+            return launch_dma_one<DmaL>(p, p.l[1], x, w, Y, yb, M, N, Kd, partial, s);
+        }
     }
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
     return SPEC_OK;

@@ -81,10 +81,25 @@ def test_between_sweep_sizes_every_element():
 
 
 def test_lmhead_every_element():
-    # the lm-head launch of the fused step (192 x 256 tiles: two whole
-    # rounds, then the remainder split along K and summed by the reduce)
+    # the lm-head launch of the fused step (a round of 192 x 512 tiles, then
+    # the remaining columns as 192 x 256 tiles split along K and summed by
+    # the reduce)
     print("[spec_verify_linear] lm-head M=192 N=151936 K=4096 fp32", flush=True)
     print(_full(192, workloads.LMHEAD_N, workloads.HIDDEN, torch.float32, seed=5))
+
+
+@pytest.mark.parametrize("M,N,K,out_dtype", [
+    # 192 x 512 tiles over a partial M tile, then one remaining 256-column
+    # tile (8 columns of it in range) split four ways along K
+    (129, 131080, 512, torch.float32),
+    # a partial last 256-column tile; K of 8 stages: the remainder unsplit
+    (160, 140000, 256, torch.bfloat16),
+    # exactly whole rounds of 192 x 512 tiles: no remainder launch
+    (192, 131072, 1024, torch.float32),
+])
+def test_wide_tile_plan_every_element(M, N, K, out_dtype):
+    print(f"[spec_verify_linear] wide tiles M={M} N={N} K={K} {out_dtype}", flush=True)
+    print(_full(M, N, K, out_dtype, seed=M + N + K))
 
 
 def test_deterministic_and_m_only():
