@@ -239,6 +239,9 @@ int spec_accept_sampled(const void* target_logits, const void* draft_logits, int
  *   workspace   device scratch of at least
  *               spec_verify_linear_workspace_bytes(M, N, Kd) bytes (may be
  *               NULL when that is 0); its contents need not be initialised.
+ *               The size is that of the current device's plan (it depends
+ *               on the device's compute-unit count): query it with the
+ *               device the call will run on current.
  * ---------------------------------------------------------------------- */
 size_t spec_verify_linear_workspace_bytes(int64_t M, int64_t N, int64_t Kd);
 
