@@ -52,7 +52,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-breakdown", action="store_true", help="time the step only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["step", "accept", "gemm", "adapt", "attn", "sampled"], default=None,
+    ap.add_argument("--only", choices=["step", "accept", "mid", "gemm", "adapt", "attn", "sampled"], default=None,
                     help="run one part only (for profiling)")
     return ap.parse_args()
 
@@ -257,6 +257,50 @@ def bench_accept_large(torch, sv, workloads, reps=60, nsets=5):
                 us_per_call=us, latency_us=lat, positions_per_call=pos, positions_per_s=pos / us * 1e6,
                 algorithmic_bytes=b, achieved_GBs=b / us * 1e-3,
                 frac_hbm=b / us * 1e-3 / HBM_PEAK_GBS)
+
+
+def bench_accept_mid(torch, sv, workloads, reps=200):
+    """The mid-size accept pass (B=8, K=4, V=32000 fp32, T=0.6, and its
+    greedy variant with T=0 and argmax drafts): 40 positions and ~5 MB of
+    logits per call, below the launch latency, so latency and positions/s
+    are what it reports."""
+    dev = torch.device("cuda:0")
+    out = []
+    for greedy in (False, True):
+        inp = workloads.mid_accept(greedy=greedy)
+        B, K1, V = inp.logits.shape
+        K = K1 - 1
+        z = inp.logits.to(dev)
+        q = None if inp.draft_probs is None else torch.from_numpy(inp.draft_probs).to(dev)
+        x = torch.from_numpy(inp.draft_tokens).to(dev)
+        L = torch.from_numpy(inp.draft_lens).to(dev)
+        ws = sv.accept_workspace(B, K, V, dev)
+        res = sv.AcceptResult(torch.empty(B, K + 1, dtype=torch.int32, device=dev),
+                              torch.empty(B, dtype=torch.int32, device=dev),
+                              torch.empty(B, K, dtype=torch.float32, device=dev),
+                              torch.empty(B, dtype=torch.int32, device=dev))
+        T = inp.temperature
+
+        def one(i):
+            sv.accept(z, q, x, L, temperature=T, seed=inp.seed, offset=i, workspace=ws, out=res)
+        for i in range(20):
+            one(i)
+        torch.cuda.synchronize()
+        t0, t1 = _events(torch, 2)
+        t0.record()
+        for i in range(reps):
+            one(i)
+        t1.record()
+        torch.cuda.synchronize()
+        us = t0.elapsed_time(t1) * 1e3 / reps
+        lat = _single_call_us(torch, one)
+        pos = int((inp.draft_lens + 1).sum())
+        out.append(dict(mode="greedy (T=0)" if greedy else "stochastic (T=0.6)", us_per_call=round(us, 2),
+                        latency_us=round(lat, 2), positions_per_call=pos,
+                        positions_per_s=round(pos / us * 1e6, 1),
+                        logits_bytes=int(B * K1 * V * 4)))
+    return dict(workload="spec_accept B=8 K=4 L=4 V=32000 fp32, z ~ N(0, 3^2), draft = z + N(0, 1)",
+                bound="launch latency (~5 MB per call)", modes=out)
 
 
 def bench_accept_sampled(torch, sv, workloads, reps=30, nsets=4):
@@ -488,6 +532,14 @@ def _cpu_rows(workloads, cores, budget_s=2.0):
                                                 0.8, 77, 0, nthreads=cores), budget_s)
     out["accept_at_scale"] = dict(value=round(pos / sec, 1), unit="verified positions/s",
                                   sample=f"8 rows of B=64 K=7 V=128256, {n} run(s), {cores} threads")
+    # the mid-size accept pass (all 8 rows, stochastic)
+    mid = workloads.mid_accept()
+    zm = mid.logits_f32()
+    pm = int((mid.draft_lens + 1).sum())
+    sec, n = _timed(lambda: oracle.spec_accept(zm, mid.draft_probs, mid.draft_tokens, mid.draft_lens,
+                                                mid.temperature, mid.seed, 0, nthreads=cores), budget_s)
+    out["accept_mid"] = dict(value=round(pm / sec, 1), unit="verified positions/s",
+                             sample=f"all 8 rows of B=8 K=4 V=32000 fp32, {n} run(s), {cores} threads")
     # the sampler-filter path (2 rows)
     zs = z[:2]
     ds = (zs[:, :7] + np.random.default_rng(4).normal(0, 1.5, zs[:, :7].shape)).astype(np.float32)
@@ -597,6 +649,9 @@ def main():
     if args.only == "gemm":
         print(json.dumps(bench_gemm_sweep(torch, sv, workloads)))
         return
+    if args.only == "mid":
+        print(json.dumps(bench_accept_mid(torch, sv, workloads)))
+        return
     if args.only == "sampled":
         print(json.dumps(bench_accept_sampled(torch, sv, workloads)))
         return
@@ -657,6 +712,7 @@ def main():
         acc["traffic_bytes"] = counted["accept_bytes"] if counted else None
         sweep = bench_gemm_sweep(torch, sv, workloads)
         line["breakdown"] = {"accept_at_scale": acc,
+                             "accept_mid": bench_accept_mid(torch, sv, workloads),
                              "accept_sampled_at_scale": bench_accept_sampled(torch, sv, workloads),
                              "gemm_sweep": sweep,
                              "verify_attention": bench_attention(torch, sv, workloads),
