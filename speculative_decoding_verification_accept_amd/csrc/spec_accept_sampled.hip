@@ -290,15 +290,20 @@ __device__ __forceinline__ void row_rounds(const T* row, int64_t V, F&& f) {
         VecRound<T> z, nz;
 #pragma unroll
         for (int u = 0; u < kU; ++u) z.r[u] = ld16((int64_t)u * kTS);
-        for (int64_t v0 = 0; v0 < nv; v0 += kStep) {
+        int64_t v0 = 0;
+        // whole rounds: every load in the row (a compile-time mask)
+        for (; v0 + kStep <= nv; v0 += kStep) {
 #pragma unroll
             for (int u = 0; u < kU; ++u) nz.r[u] = ld16(v0 + kStep + (int64_t)u * kTS);
+            f(z, std::integral_constant<uint32_t, (1u << kU) - 1u>{});
+            z = nz;
+        }
+        if (v0 < nv) {
             uint32_t ok = 0u;
 #pragma unroll
             for (int u = 0; u < kU; ++u)
                 if (v0 + (int64_t)u * kTS + t < nv) ok |= 1u << u;
             f(z, ok);
-            z = nz;
         }
     } else {
         for (int64_t j0 = 0; j0 < V; j0 += (int64_t)kTS * kU) {
@@ -451,7 +456,8 @@ __global__ __launch_bounds__(kTS) void k_stats(Args a) {
         const float lt = log2f(minp) - 1e-4f;
         float ltr = 0.f;  // lt + fl(ref c) - kref
         float gl = -INFINITY;
-        row_rounds<T, VEC>(row, V, [&](const auto& z, uint32_t ok) {
+        row_rounds<T, VEC>(row, V, [&](const auto& z, auto okc) {
+            const uint32_t ok = okc;
             constexpr int N = std::remove_reference_t<decltype(z)>::N;
             constexpr int G = N / kU;
             static_assert(N <= 64, "one candidate bit per entry of the round");
