@@ -627,8 +627,8 @@ def cpu_baseline(torch, workloads, st, budget_s=12.0):
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(the verification step shards by rows with no exchange; see the design notes)",
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
+              "(the verification step would shard by rows, with no exchange)",
               file=sys.stderr)
         sys.exit(2)
     import torch

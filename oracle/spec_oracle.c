@@ -25,8 +25,7 @@
  * the exact values the GPU receives (bf16 widens to fp32 without rounding).
  * Loops run in plain sequential index order.
  *
- * Readings of the pages taken where they are silent (each one is also listed
- * in the design notes):
+ * Readings of the pages taken where they are silent:
  *  - the acceptance ratio has no epsilon: a = min(1, p(x)/q(x)), accept iff
  *    u < a with u in [0,1);  q(x) <= 0 is a data error (ROW_ZERO_Q).
  *  - each (row, position) gets its own Philox block; word 0 drives the
