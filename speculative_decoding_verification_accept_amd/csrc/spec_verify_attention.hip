@@ -15,9 +15,11 @@
 //    verifying D drafts multiplies the rows by 1+D; here those rows share
 //    one read of the cache.
 //
-// Work: one workgroup of four waves per (KV-range split s, KV head g,
-// sequence b).  The query rows of (b, g) are R = (K+1) G (position-major,
-// then the G query heads of the group), at most 32: one or two 16-row tiles.
+// Work: one workgroup per (KV-range split s, KV head g, sequence b), of
+// eight waves for one 16-row tile of queries and four for two (the larger
+// state would spill at eight).  The query rows of (b, g) are R = (K+1) G
+// (position-major, then the G query heads of the group), at most 32: one or
+// two 16-row tiles.
 // Each wave takes 32-key steps of the split, interleaved with the other
 // waves, and keeps its own online-softmax state (running max and sum per
 // row, unnormalised output) in registers:
@@ -35,7 +37,7 @@
 // The next two steps' loads are always in flight; their key indices are
 // clamped into the split's range, so prefetches past its end re-read the
 // last row (a cache hit) instead of branching around the loads.
-// The four waves' states merge in LDS (log-sum-exp); with one split the
+// The waves' states merge in LDS (log-sum-exp); with one split the
 // workgroup writes the normalised output, else an unnormalised partial that
 // k_attn_combine merges over the splits (a fixed grouping and order).
 #include "spec_verify.h"
@@ -48,10 +50,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kD = SPEC_ATTN_HEAD_DIM;     // 128
-constexpr int kAWaves = 4;
-constexpr int kAThreads = kAWaves * kWave;
 constexpr int kStep = 32;                  // keys per wave step
-constexpr int kRound = kAWaves * kStep;    // keys per step of the whole workgroup
+// Waves of a workgroup: eight for one 16-row tile, four for two (whose
+// state needs twice the registers: at eight waves it would spill).
+template <int RT> constexpr int attn_waves() { return RT == 1 ? 8 : 4; }
 constexpr int kMaxRows = SPEC_ATTN_MAX_ROWS;
 constexpr int kSplitTarget = 256;          // workgroups a launch aims for
 constexpr int kSplitMinKeys = 256;         // keys per split at least
@@ -202,10 +204,12 @@ __device__ __forceinline__ void store_val(void* out, int bf16, int64_t idx, floa
 }
 
 template <int RT>
-__global__ __launch_bounds__(kAThreads) void k_attn(AttnArgs a) {
+__global__ __launch_bounds__(attn_waves<RT>() * kWave) void k_attn(AttnArgs a) {
     constexpr int NR = RT * 16;
-    __shared__ float sm[kAWaves][NR], sl[kAWaves][NR];
-    __shared__ float so[kAWaves][NR][kD];
+    constexpr int NWV = attn_waves<RT>(), NTH = NWV * kWave;
+    constexpr int kRound = NWV * kStep;  // keys per step of the whole workgroup
+    __shared__ float sm[NWV][NR], sl[NWV][NR];
+    __shared__ float so[NWV][NR][kD];
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t / kWave;
     const int kg = lane >> 4, li = lane & 15;
     const int s = blockIdx.x, g = blockIdx.y;
@@ -231,7 +235,7 @@ __global__ __launch_bounds__(kAThreads) void k_attn(AttnArgs a) {
         for (int e = 0; e < 8; ++e) ws.o[rt][e] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
 
-    // this wave's steps: keys lo + 32 (w + 4 n) < hi
+    // this wave's steps: keys lo + 32 (w + NWV n) < hi
     const int64_t first = lo + kStep * w;
     const int nsteps = first < hi ? (int)((hi - first + kRound - 1) / kRound) : 0;
     if (nsteps > 0) {
@@ -252,7 +256,7 @@ __global__ __launch_bounds__(kAThreads) void k_attn(AttnArgs a) {
         }
     }
 
-    // merge the four waves: running max and sum per row, scaled outputs
+    // merge the waves: running max and sum per row, scaled outputs
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         float l = ws.l[rt];
@@ -269,16 +273,16 @@ __global__ __launch_bounds__(kAThreads) void k_attn(AttnArgs a) {
     }
     __syncthreads();
     const bool direct = a.nsplit == 1;
-    for (int idx = t; idx < NR * kD; idx += kAThreads) {
+    for (int idx = t; idx < NR * kD; idx += NTH) {
         const int r = idx / kD, dim = idx % kD;
         if (r >= a.R) break;  // rows are visited in order
         float M = sm[0][r];
 #pragma unroll
-        for (int k = 1; k < kAWaves; ++k) M = fmaxf(M, sm[k][r]);
+        for (int k = 1; k < NWV; ++k) M = fmaxf(M, sm[k][r]);
         float o = 0.f, ls = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
-            for (int k = 0; k < kAWaves; ++k) {
+            for (int k = 0; k < NWV; ++k) {
                 const float f = sm[k][r] == -INFINITY ? 0.f : hw_exp2(sm[k][r] - M);
                 o += so[k][r][dim] * f;
                 ls += sl[k][r] * f;
@@ -444,8 +448,8 @@ extern "C" int spec_verify_attention(const void* q, const void* k_cache, const v
     }
     const hipStream_t st = reinterpret_cast<hipStream_t>(stream);
     const dim3 grid((unsigned)p.nsplit, (unsigned)Hkv, (unsigned)B);
-    if (a.R <= 16) hipLaunchKernelGGL(k_attn<1>, grid, dim3(kAThreads), 0, st, a);
-    else hipLaunchKernelGGL(k_attn<2>, grid, dim3(kAThreads), 0, st, a);
+    if (a.R <= 16) hipLaunchKernelGGL(k_attn<1>, grid, dim3(attn_waves<1>() * kWave), 0, st, a);
+    else hipLaunchKernelGGL(k_attn<2>, grid, dim3(attn_waves<2>() * kWave), 0, st, a);
     if (hipGetLastError() != hipSuccess) return SPEC_ERR_HIP;
     if (p.nsplit > 1) {
         const int ng = std::min(kCGroups, (p.nsplit + kCBatch - 1) / kCBatch);
