@@ -513,8 +513,10 @@ __global__ __launch_bounds__(kTS) void k_stats(Args a) {
                 sacc += (double)part;
             }
             // candidates (rare after the first rounds): an entry passes the
-            // test only if the round's max does (c > 0); one LDS atomic per
-            // wave, slots in lane order
+            // test only if the round's max does (c > 0).  Each lane holding
+            // candidates takes its slots with one LDS atomic of its own; the
+            // order of the collected entries is immaterial (the radix select's
+            // mass histograms and the kept sum over them are integer sums)
             const bool hit = mx > -INFINITY && __builtin_fmaf(r, c, -mcref) >= ltr;
             if (__ballot(hit)) {
                 const auto zc = z.fresh();
@@ -525,15 +527,8 @@ __global__ __launch_bounds__(kTS) void k_stats(Args a) {
                         in |= (((ok >> (e / G)) & 1u) && __builtin_fmaf(zc[e], c, -mcref) >= ltr ? 1ull : 0ull) << e;
                 }
                 const int mine = __popcll(in);
-                int incl = mine;
-                for (int o = 1; o < kWave; o <<= 1) {
-                    const int nb = __shfl_up(incl, o, kWave);
-                    if (lane >= o) incl += nb;
-                }
-                int base = 0;
-                if (lane == kWave - 1) base = atomicAdd(&sh.ncand, incl);
-                base = __shfl(base, kWave - 1, kWave);
-                int slot = base + incl - mine;
+                int slot = 0;
+                if (mine) slot = atomicAdd(&sh.ncand, mine);
 #pragma unroll
                 for (int e = 0; e < N; ++e)
                     if ((in >> e) & 1ull) {
