@@ -14,15 +14,16 @@
 // 8 consecutive k per lane; X (K contiguous) is used as stored.  The MFMA
 // computes D = A B with A an X fragment and B a W fragment.
 //
-//  k_strip (M <= 16, or <= 32 when K is not a multiple of 64; memory-bound):
+//  k_strip (M <= 32 when K is not a multiple of 64; memory-bound):
 //    one 512-thread workgroup per 64-column
 //    strip of W, all M rows, the full K.  Each of its 8 waves takes a slice
 //    of K, keeps 4 k-steps of W loads in flight, transposes each lane's 8x4
 //    block of W in registers (v_perm_b32) straight into
 //    v_mfma_f32_16x16x32_bf16 operands, and the waves' partial tiles are
 //    summed through LDS in a fixed order.  W streams from HBM exactly once.
-//  k_dma (M > 16, K a multiple of 32 or 64; v_mfma_f32_32x32x16_bf16): a
-//    workgroup computes a BM x BN tile.  Tiles of X and W go from HBM
+//  k_dma (K a multiple of 64, or of 32 past 32 rows; v_mfma_f32_32x32x16_bf16):
+//    a workgroup computes a BM x BN tile; BM is 32 or 64 for a few rows, so
+//    that the X rows streamed per W byte stay few.  Tiles of X and W go from HBM
 //    straight into an LDS ring of 4-5 stages by loads that write LDS, so the
 //    prefetch distance costs no registers; W stays [k][n] in LDS and the
 //    transposing LDS read ds_read_b64_tr_b16 builds its MFMA operands.
@@ -789,13 +790,15 @@ __global__ void k_reduce(const float* __restrict__ partial, void* __restrict__ Y
 using TileS = TileCfg<128, 128, 64, 32, 64>;   // 8 waves; K not a multiple of 32
 using TileL = TileCfg<192, 256, 64, 96, 64>;
 using TileB = TileCfg<256, 128, 64, 64, 64>;
-using DmaS = DmaCfg<128, 128, 64, 2, 4, 4>;   // M in (16, 128], or (128, 256] on narrow N
+using DmaS32 = DmaCfg<32, 128, 64, 1, 4, 4>;  // M <= 32
+using DmaS64 = DmaCfg<64, 128, 64, 2, 4, 4>;  // M in (32, 64]
+using DmaS = DmaCfg<128, 128, 64, 2, 4, 4>;   // M in (64, 128], or (128, 256] on narrow N
 using DmaL = DmaCfg<192, 256, 32, 2, 4, 5>;   // M in (128, 192] on a wide N (lm-head)
 using DmaW = DmaCfg<192, 512, 32, 2, 8, 3>;   // M in (128, 192], N >= 512 columns per compute unit
 using DmaB = DmaCfg<256, 128, 32, 4, 2, 5>;   // M in (256, 512]
 using DmaH = DmaCfg<256, 256, 64, 2, 4, 2>;   // M > 512, K a multiple of 64
 
-enum Kern { kStrip1, kStrip2, kTileS, kTileL, kTileB, kDmaS, kDmaL, kDmaB, kDmaH, kDmaWL };
+enum Kern { kStrip1, kStrip2, kTileS, kTileL, kTileB, kDmaS32, kDmaS64, kDmaS, kDmaL, kDmaB, kDmaH, kDmaWL };
 
 // One or two launches over ranges of n-tiles; each may split K.
 struct Launch {
@@ -813,9 +816,11 @@ struct Plan {
 
 Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
     Plan p{};
-    // the strip kernel for a few rows; from 17 rows the 128x128 tile (K a
-    // multiple of 64) measured faster on MI355X (31.4 vs 34.0 us at M = 32,
-    // N = 14336, K = 4096)
+    // the strip kernel for up to 32 rows when K is not a multiple of 64;
+    // otherwise a tile of 32 or 64 rows streams fewer X bytes per W byte
+    // than the 128-row tile and beats the strip kernel too (MI355X, N =
+    // 14336, K = 4096: M = 8: 24.2 vs 27.2 us, M = 32: 26.5 vs 33.0 us
+    // with the 128-row tile, M = 64: 29.0 vs 36.2 us)
     auto strip_plan = [&]() {
         p.kern = M <= 16 ? kStrip1 : kStrip2;
         const int mt = M <= 16 ? 1 : 2;
@@ -825,7 +830,7 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
         p.l[0] = Launch{0, p.ntiles, 1};
         return p;
     };
-    if (M <= 16 || (M <= 32 && K % 64 != 0)) return strip_plan();
+    if (M <= 32 && K % 64 != 0) return strip_plan();
     // the lm-head class (128 < M <= 192, at least one 192 x 512 tile per
     // compute unit): whole rounds of 192 x 512 tiles, then the remaining
     // columns as 192 x 256 tiles, split along K when they fill at most half
@@ -852,7 +857,11 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
     }
     int BM, BN, BK;
     auto pick = [&](Kern k, int bm, int bn, int bk) { p.kern = k; BM = bm; BN = bn; BK = bk; };
-    if (K % 64 == 0 && M <= 128) {
+    if (K % 64 == 0 && M <= 32) {
+        pick(kDmaS32, DmaS32::BM, DmaS32::BN, DmaS32::BK);
+    } else if (K % 64 == 0 && M <= 64) {
+        pick(kDmaS64, DmaS64::BM, DmaS64::BN, DmaS64::BK);
+    } else if (K % 64 == 0 && M <= 128) {
         pick(kDmaS, DmaS::BM, DmaS::BN, DmaS::BK);
     } else if (K % 32 == 0 && M <= 192 && (N + DmaL::BN - 1) / DmaL::BN >= cus) {
         pick(kDmaL, DmaL::BM, DmaL::BN, DmaL::BK);
@@ -882,7 +891,8 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
     p.ntiles = (N + BN - 1) / BN;
     const int64_t tiles = p.mtiles * p.ntiles;
     const int64_t nst = (K + BK - 1) / BK;
-    const bool dma = p.kern == kDmaS || p.kern == kDmaL || p.kern == kDmaB || p.kern == kDmaH;
+    const bool dma = p.kern == kDmaS32 || p.kern == kDmaS64 || p.kern == kDmaS || p.kern == kDmaL ||
+                     p.kern == kDmaB || p.kern == kDmaH;
     const int64_t rem = p.ntiles % cus;
     if (dma && p.mtiles == 1 && p.ntiles > cus && rem > 0 && 2 * rem <= cus && nst >= 16) {
         // whole rounds of tiles, then the remainder split along K so that
@@ -1005,6 +1015,8 @@ extern "C" int spec_verify_linear(const void* X, const void* W, void* Y, int y_d
         case kTileS: return launch_tile<TileS, 2>(p, x, w, Y, yb, M, N, Kd, partial, s);
         case kTileL: return launch_tile<TileL, 2>(p, x, w, Y, yb, M, N, Kd, partial, s);
         case kTileB: return launch_tile<TileB, 2>(p, x, w, Y, yb, M, N, Kd, partial, s);
+        case kDmaS32: return launch_dma<DmaS32>(p, x, w, Y, yb, M, N, Kd, partial, s);
+        case kDmaS64: return launch_dma<DmaS64>(p, x, w, Y, yb, M, N, Kd, partial, s);
         case kDmaS: return launch_dma<DmaS>(p, x, w, Y, yb, M, N, Kd, partial, s);
         case kDmaL: return launch_dma<DmaL>(p, x, w, Y, yb, M, N, Kd, partial, s);
         case kDmaB: return launch_dma<DmaB>(p, x, w, Y, yb, M, N, Kd, partial, s);

@@ -48,6 +48,9 @@ def _check(Y, ref, label):
     (200, 136, 128), (300, 264, 512), (600, 392, 256), (520, 1160, 320),
     # past 512 rows with K a multiple of 32 but not of 64: the 256 x 128 tile
     (600, 392, 288),
+    # the 32- and 64-row tiles: a ragged last column tile, K of 3 stages
+    # (unsplit), and 17 tiles split in two along K
+    (1, 1032, 128), (24, 520, 192), (32, 2056, 1024), (40, 1160, 192), (64, 2056, 1024),
 ])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_small_shapes_every_element(M, N, K, out_dtype):
