@@ -512,8 +512,10 @@ __global__ __launch_bounds__(kTS) void k_stats(Args a) {
             } else {
                 sacc += (double)part;
             }
-            // candidates (rare after the first rounds): an entry passes the
-            // test only if the round's max does (c > 0).  Each lane holding
+            // candidates: an entry passes the test only if the round's max
+            // does (c > 0), so the per-entry test runs only in waves where
+            // some lane's round max passes (about a third of a row's wave
+            // rounds on Gaussian logits at min-p 0.05).  Each lane holding
             // candidates takes its slots with one LDS atomic of its own; the
             // order of the collected entries is immaterial (the radix select's
             // mass histograms and the kept sum over them are integer sums)
