@@ -46,10 +46,11 @@ def _replays(capture, eager, outs, n=3):
 
 
 def test_verify_step_in_a_graph():
-    # the lm-head product (two launches and the split reduction) and the
+    # the step's lm-head product (a round of 192 x 512 tiles, the remaining
+    # columns split along K, and the reduction of their partials) and the
     # accept pass over its logits
     dev = torch.device("cuda:0")
-    B, K, V, H = 8, 3, workloads.LMHEAD_N, workloads.HIDDEN
+    B, K, V, H = 32, 5, workloads.LMHEAD_N, workloads.HIDDEN
     M = B * (K + 1)
     X, W = workloads.linear_inputs(M, H, V, seed=3, device=dev)
     logits = torch.empty(M, V, dtype=torch.float32, device=dev)
@@ -71,6 +72,23 @@ def test_verify_step_in_a_graph():
         sv.accept(z3, q, x, L, temperature=0.6, seed=5, offset=9, workspace=ws_acc, out=out)
 
     _replays(step, step, [logits, out.tokens, out.accepted, out.p_draft, out.status])
+
+
+@pytest.mark.parametrize("M", [8, 32])
+def test_small_m_linear_in_a_graph(M):
+    # the 32-row tile split in two along K, and the reduction of its partials
+    dev = torch.device("cuda:0")
+    H, N = workloads.HIDDEN, workloads.FFN_N
+    X, W = workloads.linear_inputs(M, H, N, seed=40 + M, device=dev)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    n = sv.linear_workspace_bytes(M, N, H)
+    assert n > 0  # the split-K plan needs fp32 partials
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+
+    def run():
+        sv.verify_linear(X, W, out=Y, workspace=ws)
+
+    _replays(run, run, [Y])
 
 
 def test_sampled_accept_in_a_graph():
