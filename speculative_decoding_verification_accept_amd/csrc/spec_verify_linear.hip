@@ -795,8 +795,8 @@ using DmaS64 = DmaCfg<64, 128, 64, 2, 4, 4>;  // M in (32, 64]
 using DmaS = DmaCfg<128, 128, 64, 2, 4, 4>;   // M in (64, 128], or (128, 256] on narrow N
 using DmaL = DmaCfg<192, 256, 32, 2, 4, 5>;   // M in (128, 192] on a wide N (lm-head)
 using DmaW = DmaCfg<192, 512, 32, 2, 8, 3>;   // M in (128, 192], N >= 512 columns per compute unit
-using DmaB = DmaCfg<256, 128, 32, 4, 2, 5>;   // M in (256, 512]
-using DmaH = DmaCfg<256, 256, 64, 2, 4, 2>;   // M > 512, K a multiple of 64
+using DmaB = DmaCfg<256, 128, 32, 4, 2, 5>;   // M in (256, 464]
+using DmaH = DmaCfg<256, 256, 64, 2, 4, 2>;   // M > 464, K a multiple of 64
 
 enum Kern { kStrip1, kStrip2, kTileS, kTileL, kTileB, kDmaS32, kDmaS64, kDmaS, kDmaL, kDmaB, kDmaH, kDmaWL };
 
@@ -868,11 +868,14 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
     } else if (K % 64 == 0 && M <= 256) {
         pick(kDmaS, DmaS::BM, DmaS::BN, DmaS::BK);
     } else if (K % 32 == 0 && M > 256) {
-        // past 512 rows the 256 x 256 tile: at M = 768, N = 14336 its 168
+        // past 464 rows the 256 x 256 tile: at M = 768, N = 14336 its 168
         // tiles fit one round on 256 compute units where the 336 tiles of
-        // 256 x 128 need two (measured 111 us against 152 us).  Its stage is
-        // 64 deep (half the barriers of 32: 2-3% faster at M = 768 and 1024)
-        if (M <= 512 || K % 64 != 0) pick(kDmaB, DmaB::BM, DmaB::BN, DmaB::BK);
+        // 256 x 128 need two (measured 111 us against 152 us); at M = 480-512
+        // its 112 tiles split in two along K stream fewer bytes per
+        // workgroup than 224 tiles of 256 x 128 (79.1 vs 82.4 us at M = 512,
+        // slower below 464 rows).  Its stage is 64 deep (half the barriers
+        // of 32: 2-3% faster at M = 768 and 1024)
+        if (M <= 464 || K % 64 != 0) pick(kDmaB, DmaB::BM, DmaB::BN, DmaB::BK);
         else pick(kDmaH, DmaH::BM, DmaH::BN, DmaH::BK);
     } else if (M > 128 && M <= 192 && (N + TileL::BN - 1) / TileL::BN >= cus) {
         pick(kTileL, TileL::BM, TileL::BN, TileL::BK);

@@ -51,6 +51,8 @@ def _check(Y, ref, label):
     # the 32- and 64-row tiles: a ragged last column tile, K of 3 stages
     # (unsplit), and 17 tiles split in two along K
     (1, 1032, 128), (24, 520, 192), (32, 2056, 1024), (40, 1160, 192), (64, 2056, 1024),
+    # 465-512 rows: the 256 x 256 tile over two row tiles, split in two along K
+    (480, 1032, 1024),
 ])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
 def test_small_shapes_every_element(M, N, K, out_dtype):
