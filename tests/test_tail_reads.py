@@ -4,8 +4,10 @@ operands, or read zeros where it steps past them.
 Each operand is a view into a larger allocation whose tail, right after the
 operand, is filled with NaN.  That memory is mapped, so a kernel that read
 past an operand would not fault here, but a value it took from the tail
-would turn its outputs into NaN.  The shapes put the last k-stage of the
-register-staged GEMM tile past K (K not a multiple of its 64-deep stage) and
+would turn its outputs into NaN.  The GEMM shapes reach every tile plan
+(the strip kernel, the 32-, 64-, 128-, 256- and 256x256-row tiles) with
+ragged rows and columns, and put the last k-stage of the register-staged
+tile past K (K not a multiple of its 64-deep stage); the other shapes put
 the last round of the sampler-filter row reader past the row (V not a
 multiple of a round), on the last row of the logits.
 """
@@ -43,7 +45,8 @@ def _nan_tailed(t: torch.Tensor) -> torch.Tensor:
 
 
 @pytest.mark.parametrize("M,N,K", [(65, 520, 1000), (300, 256, 520), (257, 8, 8), (40, 1032, 200),
-                                   (130, 264, 96)])
+                                   (130, 264, 96), (8, 1032, 1024), (24, 520, 200), (48, 1160, 576),
+                                   (100, 1032, 576), (300, 1032, 512), (480, 520, 512)])
 def test_gemm_operands_nan_tailed(M, N, K):
     print(f"[tail reads] spec_verify_linear M={M} N={N} K={K}", flush=True)
     X, W = workloads.linear_inputs(M, K, N, seed=M + N + K, device="cuda")
