@@ -5,7 +5,9 @@
  * The library implements the target model's verification step of
  * speculative decoding as two stages:
  *   spec_verify_linear  the verify linear layer, Y = X W, whose row count
- *                       grows from B to B(1+D) when D drafts are verified;
+ *                       grows from B to B(1+D) when D drafts are verified
+ *                       (spec_verify_linear_packed: the same with W stored
+ *                       once in the MFMA operand order by spec_pack_weight);
  *   spec_accept         the batched accept/reject pass over the target's
  *                       vocabulary distributions (spec_accept_sampled: the
  *                       same with the draft as logits and the sampler's
@@ -250,6 +252,57 @@ int spec_verify_linear(const void* X, const void* W, void* Y, int y_dtype,
                        size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * spec_pack_weight / spec_verify_linear_packed -- the same product,
+ * Y[M, N] = X[M, K] W[K, N] (bf16 operands, fp32 accumulation, Y fp32 or
+ * bf16), with W rewritten once into the operand order of the gfx950 MFMA
+ * (v_mfma_f32_16x16x32_bf16), for a weight that every verify pass reads
+ * whole, such as the lm-head.  The packed product streams W straight into
+ * registers instead of through LDS.
+ *
+ * Defined by: page "New technical post reveals how speculative decoding
+ * accelerates LLM inference without hurting accuracy" (agentnet.co.il),
+ * sections "The formula behind the speedup" and "GEMM-M grows, a small
+ * batch suffices" (as spec_verify_linear).
+ *
+ * Packed layout: 2 KB blocks, block (s, c) for k rows 32 s .. 32 s + 31 and
+ * columns 32 c .. 32 c + 31 at byte (s C + c) 2048, C = ceil(N / 32).  In a
+ * block, the 16 bytes at 16 (64 h + l), h in {0, 1}, l < 64, hold
+ * W[32 s + 8 (l / 16) + j][32 c + 16 h + l % 16] for j = 0..7.  Columns at
+ * or past N are zero.
+ *
+ * spec_packed_weight_bytes(K, N): size of the packed W; 0 for an
+ *   unsupported shape (K must be a positive multiple of 64, at most 2^30;
+ *   1 <= N <= 2^36).
+ * spec_pack_weight(W, Wp, K, N, stream): W [K, N] bf16 row-major (2-byte
+ *   aligned) into Wp (caller-owned device memory of
+ *   spec_packed_weight_bytes(K, N) bytes, 16-byte aligned); enqueued on
+ *   stream.  SPEC_ERR_INVALID_ARG for a bad shape or pointer.
+ * spec_verify_linear_packed(X, Wp, Y, y_dtype, M, N, K, workspace,
+ *   workspace_bytes, stream):
+ *   X   [M, K] bf16, row-major (K contiguous), 16-byte aligned
+ *   Wp  the packed W of the same K and N, 16-byte aligned
+ *   Y   [M, N] of y_dtype (SPEC_F32 or SPEC_BF16), 16-byte aligned
+ *   M >= 0 (M == 0 returns SPEC_OK without launching); K and N as above
+ *   (SPEC_ERR_INVALID_ARG otherwise).
+ *   workspace   device scratch of at least
+ *               spec_verify_linear_packed_workspace_bytes(M, N, K) bytes
+ *               (may be NULL when that is 0; contents need not be
+ *               initialised), 16-byte aligned, else SPEC_ERR_WORKSPACE.
+ *               The size depends on the current device's compute-unit
+ *               count: query it with that device current.
+ *   Results equal spec_verify_linear's up to the order of the fp32 sums.
+ * ---------------------------------------------------------------------- */
+size_t spec_packed_weight_bytes(int64_t K, int64_t N);
+
+int spec_pack_weight(const void* W, void* Wp, int64_t K, int64_t N, void* stream);
+
+size_t spec_verify_linear_packed_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+int spec_verify_linear_packed(const void* X, const void* Wp, void* Y, int y_dtype,
+                              int64_t M, int64_t N, int64_t K, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * spec_adapt -- acceptance telemetry and the adaptive draft depth, run on
  * the GPU after a verify pass, from that pass's out_accepted.
  *
@@ -419,7 +472,7 @@ int spec_debug_set_wait_bound(int polls);
 const char* spec_status_string(int code);
 
 /* ABI version of this header (incremented on incompatible changes). */
-#define SPEC_VERIFY_ABI_VERSION 3
+#define SPEC_VERIFY_ABI_VERSION 4
 int spec_abi_version(void);
 
 #ifdef __cplusplus

@@ -65,6 +65,11 @@ ABI = [
     ("spec_verify_linear_workspace_bytes", ctypes.c_size_t, [_I64, _I64, _I64]),
     ("spec_verify_linear", ctypes.c_int,
      [_P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
+    ("spec_packed_weight_bytes", ctypes.c_size_t, [_I64, _I64]),
+    ("spec_pack_weight", ctypes.c_int, [_P, _P, _I64, _I64, _P]),
+    ("spec_verify_linear_packed_workspace_bytes", ctypes.c_size_t, [_I64, _I64, _I64]),
+    ("spec_verify_linear_packed", ctypes.c_int,
+     [_P, _P, _P, ctypes.c_int, _I64, _I64, _I64, _P, ctypes.c_size_t, _P]),
     ("spec_verify_attention_workspace_bytes", ctypes.c_size_t,
      [_I64, ctypes.c_int, ctypes.c_int, ctypes.c_int, _I64]),
     ("spec_verify_attention", ctypes.c_int,
@@ -301,6 +306,69 @@ def verify_linear(X, W, *, out=None, out_dtype=torch.float32, workspace=None, st
                                 nbytes, _stream(stream))
     if rc != SPEC_OK:
         raise SpecError("spec_verify_linear", rc)
+    return out
+
+
+def linear_packed_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(load_library().spec_verify_linear_packed_workspace_bytes(M, N, K))
+
+
+def packed_weight_bytes(K: int, N: int) -> int:
+    """Bytes of W [K, N] in the packed layout (``spec_packed_weight_bytes``;
+    0 for an unsupported shape)."""
+    return int(load_library().spec_packed_weight_bytes(K, N))
+
+
+def pack_weight(W, *, out=None, stream=None):
+    """W [K, N] bfloat16 (input-major) rewritten into the MFMA operand order
+    (``spec_pack_weight``); returns a uint8 tensor of packed_weight_bytes(K, N)."""
+    _check_dev("W", W, torch.bfloat16, 2)
+    K, N = W.shape
+    nbytes = packed_weight_bytes(K, N)
+    if nbytes == 0:
+        raise ValueError(f"unsupported shape for the packed layout: K={K}, N={N} "
+                         "(K must be a positive multiple of 64)")
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=W.device)
+    _check_dev("out", out)
+    if out.numel() * out.element_size() < nbytes:
+        raise ValueError("out is smaller than the packed weight")
+    rc = load_library().spec_pack_weight(_ptr(W), _ptr(out), K, N, _stream(stream))
+    if rc != SPEC_OK:
+        raise SpecError("spec_pack_weight", rc)
+    return out
+
+
+def verify_linear_packed(X, Wp, N: int, *, out=None, out_dtype=torch.float32, workspace=None,
+                         stream=None):
+    """Y = X W with W packed by pack_weight (``spec_verify_linear_packed``).
+
+    X [M, K] bfloat16, Wp the packed W [K, N], Y [M, N] float32 or bfloat16.
+    """
+    _check_dev("X", X, torch.bfloat16, 2)
+    _check_dev("Wp", Wp)
+    M, K = X.shape
+    nbytes = packed_weight_bytes(K, N)
+    if nbytes == 0 or Wp.numel() * Wp.element_size() < nbytes:
+        raise ValueError("Wp does not hold a packed weight of this K and N")
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=X.device)
+    _check_dev("out", out, None, 2)
+    if out.dtype == torch.float32:
+        yd = SPEC_F32
+    elif out.dtype == torch.bfloat16:
+        yd = SPEC_BF16
+    else:
+        raise TypeError("out must be float32 or bfloat16")
+    lib = load_library()
+    need = lib.spec_verify_linear_packed_workspace_bytes(M, N, K)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = lib.spec_verify_linear_packed(_ptr(X), _ptr(Wp), _ptr(out), yd, M, N, K, _ptr(workspace),
+                                       wsb, _stream(stream))
+    if rc != SPEC_OK:
+        raise SpecError("spec_verify_linear_packed", rc)
     return out
 
 

@@ -38,6 +38,7 @@ PER_FILE = {
     "spec_accept.hip": ["-ffp-contract=off", *NO_ATOMIC_OPT],
     "spec_accept_sampled.hip": ["-ffp-contract=off", *NO_ATOMIC_OPT],
     "spec_verify_linear.hip": [],
+    "spec_verify_linear_packed.hip": [],
     "spec_adapt.hip": ["-ffp-contract=off"],
     "spec_plan.cpp": ["-ffp-contract=off"],
     "api.cpp": [],

@@ -9,6 +9,10 @@ namespace specv {
 
 constexpr int kWave = 64;
 
+// Host: compute units of the current device (queried once per device and
+// cached; the GEMM plans depend on it).  Defined in spec_verify_linear.hip.
+int device_cus();
+
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // bf16 is the top half of an fp32: widening is a shift / mask, exact.

@@ -916,25 +916,6 @@ Plan make_plan(int64_t M, int64_t N, int64_t K, int cus) {
     return p;
 }
 
-// Compute units of the current device, queried once per device and cached
-// (the plan depends on it; a query per call would cost a runtime round trip).
-constexpr int kMaxDevices = 64;
-std::atomic<int> g_cus[kMaxDevices];
-
-int device_cus() {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (dev >= 0 && dev < kMaxDevices) {
-        const int c = g_cus[dev].load(std::memory_order_relaxed);
-        if (c > 0) return c;
-    }
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 256;
-    cus = cus > 0 ? cus : 256;
-    if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(cus, std::memory_order_relaxed);
-    return cus;
-}
-
 // NP: row stride of the partials, covering columns l.t0 BN .. l.t0 BN + NP - 1.
 int launch_reduce(const Launch& l, int BN, int64_t NP, float* partial, void* Y, int yb, int64_t M,
                   int64_t N, hipStream_t s) {
@@ -984,7 +965,27 @@ int launch_dma(const Plan& p, const uint16_t* x, const uint16_t* w, void* Y, int
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+
 }  // namespace
+
+// Compute units of the current device, queried once per device and cached
+// (the plans depend on it; a query per call would cost a runtime round trip).
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int c = g_cus[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 256;
+    cus = cus > 0 ? cus : 256;
+    if (dev >= 0 && dev < kMaxDevices) g_cus[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
 }  // namespace specv
 
 using namespace specv;

@@ -35,14 +35,16 @@ def test_header_declares_the_boundary():
                           "spec_adapt_telemetry_bytes", "spec_plan_depth",
                           "spec_verify_attention", "spec_verify_attention_workspace_bytes",
                           "spec_accept_sampled", "spec_accept_sampled_workspace_bytes",
-                          "spec_debug_set_wait_bound", "spec_accept_noalloc"]), fns
+                          "spec_debug_set_wait_bound", "spec_accept_noalloc",
+                          "spec_packed_weight_bytes", "spec_pack_weight",
+                          "spec_verify_linear_packed", "spec_verify_linear_packed_workspace_bytes"]), fns
     assert sorted(n for n, _, _ in sv.ABI) == fns
 
 
 def test_library_exports_every_declared_symbol(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.spec_abi_version() == 3
+    assert lib.spec_abi_version() == 4
     assert sv.status_string(0) == "ok"
     assert "invalid" in sv.status_string(-1)
 
@@ -244,3 +246,32 @@ def test_wait_bound_control(lib):
     assert lib.spec_debug_set_wait_bound(-1) == sv.SPEC_ERR_INVALID_ARG
     assert lib.spec_debug_set_wait_bound(5) == sv.SPEC_OK
     assert lib.spec_debug_set_wait_bound(0) == sv.SPEC_OK
+
+
+def test_packed_weight_sizes_and_validation(lib):
+    E = sv.SPEC_ERR_INVALID_ARG
+    # 2 KB per (32 rows of k, 32 columns), columns rounded up to 32
+    assert lib.spec_packed_weight_bytes(4096, 151936) == 4096 * 151936 * 2
+    assert lib.spec_packed_weight_bytes(64, 1) == 2 * 1 * 2048
+    assert lib.spec_packed_weight_bytes(128, 33) == 4 * 2 * 2048
+    for K, N in ((0, 8), (32, 8), (100, 8), (64, 0), (-64, 8)):
+        assert lib.spec_packed_weight_bytes(K, N) == 0, (K, N)
+        assert lib.spec_pack_weight(FAKE, FAKE, K, N, None) == E, (K, N)
+    assert lib.spec_pack_weight(None, FAKE, 64, 8, None) == E
+    assert lib.spec_pack_weight(FAKE, FAKE_ODD, 64, 8, None) == E
+    assert lib.spec_verify_linear_packed_workspace_bytes(0, 8, 64) == 0
+    assert lib.spec_verify_linear_packed_workspace_bytes(4, 8, 100) == 0
+
+    def run(**kw):
+        a = dict(X=FAKE, Wp=FAKE, Y=FAKE, yd=0, M=4, N=8, K=64, ws=FAKE, wsb=1 << 30, st=None)
+        a.update(kw)
+        return lib.spec_verify_linear_packed(a["X"], a["Wp"], a["Y"], a["yd"], a["M"], a["N"], a["K"],
+                                             a["ws"], a["wsb"], a["st"])
+    assert run(M=-1) == E
+    assert run(K=96) == E
+    assert run(N=0) == E
+    assert run(yd=7) == E
+    assert run(X=None) == E
+    assert run(Wp=FAKE_ODD) == E
+    assert run(Y=FAKE_ODD) == E
+    assert run(M=0) == sv.SPEC_OK

@@ -1,7 +1,8 @@
 """The fused verify step at its full size, end to end on the GPU, against the
 oracle: the verify linear layer on the lm-head (hidden [192, 4096] bf16 x
-W [4096, 151936] bf16 -> fp32 logits), then spec_accept on those logits
-(B = 32, K = 5, T = 0.6), the launch configuration the benchmark times.
+W [4096, 151936] bf16 -> fp32 logits, with W as stored and with W packed in
+the MFMA operand order, the form the benchmark times), then spec_accept on
+those logits (B = 32, K = 5, T = 0.6).
 
 Definition: page "Speculative decoding and early exit: accelerated
 autoregressive decoding" (reactapp.top), section "Speculative decoding:
@@ -62,12 +63,16 @@ def _step_inputs(seed, draft_seed, ragged=False):
     return hidden, W, logits, ws, g
 
 
-@pytest.mark.parametrize("ragged", [False, True])
-def test_fused_step_against_oracle(ragged):
+@pytest.mark.parametrize("ragged,packed", [(False, False), (True, False), (False, True)])
+def test_fused_step_against_oracle(ragged, packed):
     print(f"[fused step] lm-head GEMM + spec_accept B={B} K={K} V={workloads.LMHEAD_N} T={T} "
-          f"ragged={ragged}", flush=True)
+          f"ragged={ragged} packed={packed}", flush=True)
     hidden, W, logits, ws_lin, g = _step_inputs(5, 2005 + ragged)
-    sv.verify_linear(hidden, W, out=logits, workspace=ws_lin)
+    if packed:
+        # the benchmark's form: W stored once in the MFMA operand order
+        sv.verify_linear_packed(hidden, sv.pack_weight(W), W.shape[1], out=logits)
+    else:
+        sv.verify_linear(hidden, W, out=logits, workspace=ws_lin)
     z3 = logits.view(B, K + 1, -1)
     q, x, L = workloads.draft_side_device(z3, K, 1.0, T, g, ragged=ragged)
     ws_acc = sv.accept_workspace(B, K, z3.shape[2], z3.device)

@@ -59,6 +59,23 @@ def test_gemm_operands_nan_tailed(M, N, K):
         check_full(Y, ref, (M, N, K, dt))
 
 
+@pytest.mark.parametrize("M,N,K", [(5, 70, 128), (65, 1032, 576), (130, 300, 64), (200, 520, 512)])
+def test_packed_gemm_operands_nan_tailed(M, N, K):
+    print(f"[tail reads] spec_verify_linear_packed M={M} N={N} K={K}", flush=True)
+    X, W = workloads.linear_inputs(M, K, N, seed=M + N + K, device="cuda")
+    Wp = sv.pack_weight(W)
+    Wpt = torch.full((Wp.numel() + 2 * TAIL,), 0xFF, dtype=torch.uint8, device="cuda")  # bf16 NaN
+    Wpt = Wpt[: Wp.numel()]
+    Wpt.copy_(Wp)
+    Xt = _nan_tailed(X)
+    for dt in (torch.float32, torch.bfloat16):
+        Y = sv.verify_linear_packed(Xt, Wpt, N, out_dtype=dt)
+        torch.cuda.synchronize()
+        assert torch.isfinite(Y).all(), (M, N, K, dt)
+        ref = oracle.verify_linear(X.float().cpu().numpy(), W.float().cpu().numpy())
+        check_full(Y, ref, (M, N, K, dt))
+
+
 @pytest.mark.parametrize("V,bf16", [(20000, True), (12291, False), (8200, True), (40000, False)])
 @pytest.mark.parametrize("top_p,min_p", [(0.95, 0.05), (0.9, 0.0), (1.0, 0.05)])
 def test_sampled_rows_nan_tailed(V, bf16, top_p, min_p):

@@ -17,6 +17,7 @@ def _csv(path, rows):
 def test_summarize_scales_by_the_copy(tmp_path):
     copy = "__amd_rocclr_copyBuffer"
     dma = "void specv::(anonymous namespace)::k_dma<specv::DmaCfg<1,2> >(int)"
+    pk = "void specv::(anonymous namespace)::k_packed<12>(int)"
     acc = "void specv::(anonymous namespace)::k_accept<unsigned short, true, false>(Args)"
     kib = traffic.COPY_BYTES // 1024
     fetch = [
@@ -26,12 +27,14 @@ def test_summarize_scales_by_the_copy(tmp_path):
         {"Dispatch_Id": 2, "Kernel_Name": dma, "Grid_Size": 64, "Counter_Value": 100},
         {"Dispatch_Id": 3, "Kernel_Name": dma, "Grid_Size": 64, "Counter_Value": 300},
         {"Dispatch_Id": 4, "Kernel_Name": acc, "Grid_Size": 32, "Counter_Value": 50},
+        {"Dispatch_Id": 5, "Kernel_Name": pk, "Grid_Size": 512, "Counter_Value": 70},
     ]
     write = [
         {"Dispatch_Id": 1, "Kernel_Name": copy, "Grid_Size": 4096, "Counter_Value": kib},
         {"Dispatch_Id": 2, "Kernel_Name": dma, "Grid_Size": 64, "Counter_Value": 10},
         {"Dispatch_Id": 3, "Kernel_Name": dma, "Grid_Size": 64, "Counter_Value": 10},
         {"Dispatch_Id": 4, "Kernel_Name": acc, "Grid_Size": 32, "Counter_Value": 1},
+        {"Dispatch_Id": 5, "Kernel_Name": pk, "Grid_Size": 512, "Counter_Value": 3},
     ]
     _csv(tmp_path / "f.csv", fetch)
     _csv(tmp_path / "w.csv", write)
@@ -40,7 +43,9 @@ def test_summarize_scales_by_the_copy(tmp_path):
     launch = res["launches"]["k_dma<specv::DmaCfg<1,2> > grid=64"]
     assert launch["dispatches"] == 2
     assert launch["bytes"] == 200 * 1024 * 2 + 10 * 1024
-    assert res["calls"]["lmhead"]["bytes"] == launch["bytes"]
+    assert res["calls"]["lmhead_stored_w"]["bytes"] == launch["bytes"]
+    # the lm-head call the benchmark times is the packed-weight product
+    assert res["calls"]["lmhead"]["bytes"] == 70 * 1024 * 2 + 3 * 1024
     assert res["calls"]["accept"]["bytes"] == 50 * 1024 * 2 + 1024
 
 

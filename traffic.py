@@ -8,7 +8,8 @@ It launches, on synthetic inputs already resident on the GPU:
   * a plain device-to-device copy of 256 MiB (``copy``), the calibration of
     the byte counters against a transfer of known size;
   * the lm-head verify GEMM, hidden [192, 4096] x W [4096, 151936] bf16 ->
-    fp32 (``lmhead``);
+    fp32 (``lmhead``), with W packed in the MFMA operand order (the form the
+    benchmark times) and then from W as stored;
   * the accept/reject pass at B=64, K=7, V=128256 bf16 (``accept``).
 Each is launched ``--reps`` times after one warm-up.  ``summarize`` turns the
 profiler's counter CSVs of a FETCH_SIZE run and a WRITE_SIZE run into
@@ -32,8 +33,8 @@ PKG = os.path.join(ROOT, "speculative_decoding_verification_accept_amd")
 def source_digest() -> str:
     """SHA-256 over the HIP sources and header the counters describe."""
     h = hashlib.sha256()
-    for rel in ("csrc/spec_verify_linear.hip", "csrc/spec_accept.hip", "csrc/device_common.hpp",
-                "csrc/philox.hpp", "../include/spec_verify.h"):
+    for rel in ("csrc/spec_verify_linear.hip", "csrc/spec_verify_linear_packed.hip", "csrc/spec_accept.hip",
+                "csrc/device_common.hpp", "csrc/philox.hpp", "../include/spec_verify.h"):
         with open(os.path.join(PKG, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -54,14 +55,23 @@ def run(which, reps):
         torch.cuda.synchronize()
         del a, b
     if "lmhead" in which:
-        X, W = workloads.linear_inputs(192, workloads.HIDDEN, workloads.LMHEAD_N, seed=5, device=dev)
-        Y = torch.empty(192, workloads.LMHEAD_N, dtype=torch.float32, device=dev)
-        need = sv.linear_workspace_bytes(192, workloads.LMHEAD_N, workloads.HIDDEN)
+        M, H, V = 192, workloads.HIDDEN, workloads.LMHEAD_N
+        X, W = workloads.linear_inputs(M, H, V, seed=5, device=dev)
+        Y = torch.empty(M, V, dtype=torch.float32, device=dev)
+        # the benchmark's form: W packed once in the MFMA operand order
+        Wp = sv.pack_weight(W)
+        need = sv.linear_packed_workspace_bytes(M, V, H)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        for _ in range(reps + 1):
+            sv.verify_linear_packed(X, Wp, V, out=Y, workspace=ws)
+        torch.cuda.synchronize()
+        # and from W as stored
+        need = sv.linear_workspace_bytes(M, V, H)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
         for _ in range(reps + 1):
             sv.verify_linear(X, W, out=Y, workspace=ws)
         torch.cuda.synchronize()
-        del X, W, Y, ws
+        del X, W, Wp, Y, ws
     if "accept" in which:
         z, q, x, L = workloads.large_accept_device(3000, dev)
         ws = sv.accept_workspace(64, 7, 128256, dev)
@@ -118,7 +128,8 @@ def summarize(fetch_csv, write_csv):
             res["launches"][f"{_short(name)} grid={grid}"] = {
                 "dispatches": n, "fetch_kib": mean, "write_kib": w,
                 "bytes": mean * 1024 * kf + w * 1024 * kw}
-    for call, needles in (("lmhead", ("k_dma", "k_reduce", "k_tile", "k_strip")), ("accept", ("k_accept",))):
+    for call, needles in (("lmhead", ("k_packed",)), ("lmhead_stored_w", ("k_dma", "k_reduce", "k_tile", "k_strip")),
+                          ("accept", ("k_accept",))):
         f, w = _sum_kib(fetch, needles), _sum_kib(write, needles)
         res["calls"][call] = {"fetch_bytes": f * 1024 * kf, "write_bytes": w * 1024 * kw,
                               "bytes": f * 1024 * kf + w * 1024 * kw}
