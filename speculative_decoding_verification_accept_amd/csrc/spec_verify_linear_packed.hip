@@ -251,19 +251,35 @@ __global__ __launch_bounds__(kPkThreads) void k_packed(const uint16_t* __restric
 }
 
 // Y[r, n0 + j] = sum over the splits, in split order, of partial[s][r][j]
-// (j < ncols).
+// (j < ncols); four columns per thread when N is a multiple of 4 (n0 and the
+// partials' row stride always are).
+template <bool VEC>
 __global__ __launch_bounds__(256) void k_packed_reduce(const float* __restrict__ partial, void* __restrict__ Y,
                                                        int y_bf16, int64_t M, int64_t N, int64_t n0, int64_t ncols,
                                                        int64_t ncolP, int splits) {
+    constexpr int V = VEC ? 4 : 1;
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= M * ncols) return;
-    const int64_t r = i / ncols, j = i % ncols;
-    float v = partial[r * ncolP + j];
-    for (int s = 1; s < splits; ++s) v += partial[(s * M + r) * ncolP + j];
-    if (y_bf16)
-        static_cast<uint16_t*>(Y)[r * N + n0 + j] = f32_to_bf16(v);
-    else
-        static_cast<float*>(Y)[r * N + n0 + j] = v;
+    const int64_t per_row = ncols / V;
+    if (i >= M * per_row) return;
+    const int64_t r = i / per_row, j = V * (i % per_row);
+    if constexpr (VEC) {
+        f32x4_t v = *reinterpret_cast<const f32x4_t*>(partial + r * ncolP + j);
+        for (int s = 1; s < splits; ++s) v += *reinterpret_cast<const f32x4_t*>(partial + (s * M + r) * ncolP + j);
+        const int64_t o = r * N + n0 + j;
+        if (y_bf16)
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + o) =
+                make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                           (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+        else
+            *reinterpret_cast<f32x4_t*>(static_cast<float*>(Y) + o) = v;
+    } else {
+        float v = partial[r * ncolP + j];
+        for (int s = 1; s < splits; ++s) v += partial[(s * M + r) * ncolP + j];
+        if (y_bf16)
+            static_cast<uint16_t*>(Y)[r * N + n0 + j] = f32_to_bf16(v);
+        else
+            static_cast<float*>(Y)[r * N + n0 + j] = v;
+    }
 }
 
 // One thread per 16-byte lane record of the packed layout.
@@ -333,9 +349,15 @@ int launch_packed(const PkPlan& p, const uint16_t* x, const uint4* wp, void* Y, 
                            dim3(kPkThreads), 0, s, x, wp, Y, yb, partial, M, N, K, l.t0, l.splits, ncolP);
         if (l.splits > 1) {
             const int64_t n0 = l.t0 * kPkCols, ncols = (N < l.t1 * kPkCols ? N : l.t1 * kPkCols) - n0;
-            const int64_t n = M * ncols;
-            hipLaunchKernelGGL(k_packed_reduce, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, partial, Y, yb,
-                               M, N, n0, ncols, ncolP, l.splits);
+            if (N % 4 == 0) {
+                const int64_t n = M * (ncols / 4);
+                hipLaunchKernelGGL(k_packed_reduce<true>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                                   partial, Y, yb, M, N, n0, ncols, ncolP, l.splits);
+            } else {
+                const int64_t n = M * ncols;
+                hipLaunchKernelGGL(k_packed_reduce<false>, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                                   partial, Y, yb, M, N, n0, ncols, ncolP, l.splits);
+            }
         }
     }
     return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_ERR_HIP;

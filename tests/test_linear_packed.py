@@ -12,7 +12,8 @@ by element against the oracle (tolerance of linear_check: 1e-2 of
 max(|y|, rms), relative Frobenius error below 5e-3).
 
 The shapes reach the 64-, 128- and 192-row tiles, several row tiles, split
-and unsplit plans, ragged rows and columns, and the lm-head in the launch
+and unsplit plans (the split sums four columns per thread when N is a
+multiple of 4, one otherwise), ragged rows and columns, and the lm-head in the launch
 configuration the benchmark times (two whole rounds of tiles, the remaining
 tiles split three ways along K, their reduce).
 """
@@ -64,7 +65,7 @@ def test_pack_matches_the_layout_definition(K, N):
 SHAPES = [
     (1, 8, 64), (5, 70, 128), (17, 300, 192), (64, 520, 576), (65, 1032, 256),
     (100, 264, 640), (128, 2056, 512), (129, 1000, 64), (192, 2056, 1024), (193, 520, 128),
-    (250, 777, 320), (400, 264, 512),
+    (250, 777, 320), (400, 264, 512), (40, 777, 512), (3, 514, 1024),
 ]
 
 
