@@ -61,6 +61,18 @@ int main() {
     EXPECT(spec_verify_linear(p, p, p, SPEC_F32, 0, 16, 64, nullptr, 0, nullptr), SPEC_OK);
     EXPECT(spec_verify_linear(p, p, p, SPEC_F32, -1, 16, 64, nullptr, 0, nullptr), INV);
 
+    // spec_pack_weight / spec_verify_linear_packed
+    EXPECT((int)spec_packed_weight_bytes(96, 16), 0);                                          // K % 64
+    EXPECT((int)spec_packed_weight_bytes(128, 33), 4 * 2 * 2048);
+    EXPECT(spec_pack_weight(p, p, 96, 16, nullptr), INV);
+    EXPECT(spec_pack_weight(p, p, 64, 0, nullptr), INV);
+    EXPECT(spec_pack_weight(p, buf + 2, 64, 16, nullptr), INV);
+    EXPECT(spec_verify_linear_packed(p, p, p, SPEC_F32, 4, 16, 96, nullptr, 0, nullptr), INV);  // K % 64
+    EXPECT(spec_verify_linear_packed(p, p, p, 9, 4, 16, 64, nullptr, 0, nullptr), INV);
+    EXPECT(spec_verify_linear_packed(buf + 2, p, p, SPEC_F32, 4, 16, 64, nullptr, 0, nullptr), INV);
+    EXPECT(spec_verify_linear_packed(p, p, p, SPEC_F32, 0, 16, 64, nullptr, 0, nullptr), SPEC_OK);
+    EXPECT(spec_verify_linear_packed(p, p, p, SPEC_F32, -1, 16, 64, nullptr, 0, nullptr), INV);
+
     // spec_verify_attention
     EXPECT(spec_verify_attention(p, p, p, ip, ip, 2, 3, 32, 8, 100, 64, 0.1f, p, SPEC_F32, op, p, 4096, nullptr), INV);
     EXPECT(spec_verify_attention(p, p, p, ip, ip, 2, 3, 32, 5, 100, 128, 0.1f, p, SPEC_F32, op, p, 4096, nullptr), INV);

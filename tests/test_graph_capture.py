@@ -91,6 +91,24 @@ def test_small_m_linear_in_a_graph(M):
     _replays(run, run, [Y])
 
 
+def test_packed_lmhead_in_a_graph():
+    # the packed-weight lm-head product the step times: two rounds of tiles,
+    # the remaining tiles split along K, and the reduction of their partials
+    dev = torch.device("cuda:0")
+    M, H, V = 192, workloads.HIDDEN, workloads.LMHEAD_N
+    X, W = workloads.linear_inputs(M, H, V, seed=45, device=dev)
+    Wp = sv.pack_weight(W)
+    Y = torch.empty(M, V, dtype=torch.float32, device=dev)
+    n = sv.linear_packed_workspace_bytes(M, V, H)
+    assert n > 0
+    ws = torch.empty(n, dtype=torch.uint8, device=dev)
+
+    def run():
+        sv.verify_linear_packed(X, Wp, V, out=Y, workspace=ws)
+
+    _replays(run, run, [Y])
+
+
 def test_sampled_accept_in_a_graph():
     dev = torch.device("cuda:0")
     z, d, x, L = workloads.sampled_accept_device(7, dev, B=16, K=5, V=32768)
