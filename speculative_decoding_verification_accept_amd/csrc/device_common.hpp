@@ -50,4 +50,24 @@ __device__ __forceinline__ int wave_or(int v) {
     return v;
 }
 
+// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt untouched): at most N of this wave's
+// vector memory operations still outstanding, no LDS/scalar ones.
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// 16 bytes per lane from global memory into LDS at (M0 + 16 lane): the GEMM
+// kernels' loads that write LDS (global_load_lds_dwordx4).  Issued as inline
+// assembly: the compiler neither tracks these loads nor inserts waits for
+// them, so every wait on them is explicit (wait_vm_lgkm).  M0 holds the LDS
+// base of the load; that is sound only while the compiler keeps no value of
+// its own in M0 in the kernels that use it: in their gfx950 assembly every M0
+// access is one of these writes, one per load (checked on every build of the
+// test suite, tests/test_isa_m0.py).
+__device__ __forceinline__ void lds_dma16(const char* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
+}
+
 }  // namespace specv

@@ -548,14 +548,6 @@ __device__ __forceinline__ uint2 lds_tr16(const char* p) {
                                          (s16x4_t __attribute__((address_space(3)))*)(p)));
 }
 
-// s_waitcnt vmcnt(N) lgkmcnt(0) (expcnt untouched): at most N of this wave's
-// vector memory operations still outstanding, no LDS/scalar ones.
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
 template <typename Cfg>
 struct DmaAddr {
     const char* src[Cfg::LMAX];  // per-lane source of each load at stage 0
@@ -563,19 +555,9 @@ struct DmaAddr {
 };
 
 // Global -> LDS loads of the stage at k0 into slot D: lane l of load j writes
-// bytes [1024 j + 16 l, + 16) of the slot.  Lanes whose row or column lies
-// outside the matrix read the matrix's first bytes instead; their products
-// only reach outputs that are never stored.
-// 16 bytes per lane from global memory into LDS at (M0 + 16 lane).  Issued
-// as inline assembly: the compiler neither tracks these loads nor inserts
-// waits for them, so every wait on them is explicit (wait_vm_lgkm).
-__device__ __forceinline__ void lds_dma16(const char* src, uint32_t lds_base) {
-    // M0 holds the LDS base of the load.  Sound only while the compiler keeps
-    // no value of its own in M0 in these kernels: in the gfx950 assembly every
-    // M0 access of a k_dma instantiation is one of these writes, one per load
-    // (checked on every build of the test suite, tests/test_isa_m0.py).
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
-}
+// bytes [1024 j + 16 l, + 16) of the slot (lds_dma16).  Lanes whose row or
+// column lies outside the matrix read the matrix's first bytes instead; their
+// products only reach outputs that are never stored.
 template <typename Cfg, int D>
 __device__ __forceinline__ uint32_t slot_lds_addr() {
     return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)ring_slot<Cfg, D>();

@@ -54,21 +54,6 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
                                                    c, 0, 0, 0);
 }
 
-// 16 bytes per lane from global memory into LDS at (M0 + 16 lane), from
-// inline assembly: the compiler neither tracks these loads nor waits for
-// them, so every wait on them is explicit.  Sound only while the compiler
-// keeps no value of its own in M0 in these kernels (checked on the gfx950
-// assembly by the test suite, tests/test_isa_m0.py).
-__device__ __forceinline__ void lds_dma16(const char* src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_base), "v"(src) : "memory", "m0");
-}
-// s_waitcnt vmcnt(N) lgkmcnt(0)
-template <int N>
-__device__ __forceinline__ void wait_vm_lgkm() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
-}
-
 // X stage slot: MB x 16 rows of 128 bytes (64 k); the 16-byte group g of
 // row r sits at group g ^ ((r >> 1) & 7), which spreads the A-operand reads
 // (16 rows at one k offset) over the banks.
