@@ -65,7 +65,7 @@ def test_pack_matches_the_layout_definition(K, N):
 SHAPES = [
     (1, 8, 64), (5, 70, 128), (17, 300, 192), (64, 520, 576), (65, 1032, 256),
     (100, 264, 640), (128, 2056, 512), (129, 1000, 64), (192, 2056, 1024), (193, 520, 128),
-    (250, 777, 320), (400, 264, 512), (40, 777, 512), (3, 514, 1024),
+    (250, 777, 320), (400, 264, 512), (40, 777, 512), (3, 514, 1024), (7, 1, 64), (1000, 264, 128),
 ]
 
 
