@@ -491,35 +491,6 @@ struct DmaCfg {
     static_assert(LDS <= 160 * 1024, "LDS");
 };
 
-// Reads of register v from lane l ^ 1 and l ^ 2 of the same quad (DPP quad
-// permutations 1,0,3,2 and 2,3,0,1).
-__device__ __forceinline__ float quad_xor1(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float quad_xor2(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-}
-// 4 x 4 transpose inside each quad of lanes: lane i (qi = lane & 3) holds
-// column i of a block in v[0..3] (v[r] = row r) and ends holding row i
-// (v[c] = column c).  Two exchanges: across lane bit 0 the registers whose
-// bit 0 differs from the lane's, then across lane bit 1 likewise.  Every
-// lane of the wave must take part.
-__device__ __forceinline__ void quad_transpose(float (&v)[4], int qi) {
-    const bool b0 = qi & 1, b1 = (qi & 2) != 0;
-    const float r01 = quad_xor1(b0 ? v[0] : v[1]);
-    const float r23 = quad_xor1(b0 ? v[2] : v[3]);
-    v[0] = b0 ? r01 : v[0];
-    v[1] = b0 ? v[1] : r01;
-    v[2] = b0 ? r23 : v[2];
-    v[3] = b0 ? v[3] : r23;
-    const float r02 = quad_xor2(b1 ? v[0] : v[2]);
-    const float r13 = quad_xor2(b1 ? v[1] : v[3]);
-    v[0] = b1 ? r02 : v[0];
-    v[2] = b1 ? v[2] : r02;
-    v[1] = b1 ? r13 : v[1];
-    v[3] = b1 ? v[3] : r13;
-}
-
 // Physical 16-byte group of logical group g in X row r (BK = 32: 4 groups of
 // 64-byte rows; BK = 64: 8 groups of 128-byte rows), and in W row kr.
 template <int XG>

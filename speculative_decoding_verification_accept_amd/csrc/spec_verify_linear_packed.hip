@@ -211,26 +211,47 @@ __global__ __launch_bounds__(kPkThreads) void k_packed(const uint16_t* __restric
 #undef PK_LDW
 #undef PK_DMAX
 
-    if (c >= C) return;
-    // D register j of lane l: row 4 (l / 16) + j, column l % 16 of the block
-    const int64_t ncol = 32 * c + (lane & 15);
+    if (c >= C) return;  // wave-uniform: the quad exchanges below stay within a wave
+    // D register j of lane l: row 4 (l / 16) + j, column l % 16 of the block.
+    // With N a multiple of 4, the 4 x 4 block of a quad of lanes (lane i:
+    // column i) is transposed inside the quad (lane i: row i), so each lane
+    // stores 4 consecutive columns with one 16-byte store (8 for bf16): all
+    // four are in range or none.  Otherwise one 4-byte store per element.
+    const bool vec = (N & 3) == 0;
+    const int g = lane >> 4, qi = lane & 3;
 #pragma unroll
     for (int rb = 0; rb < MB; ++rb)
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int64_t n = ncol + 16 * h;
+            float v[4] = {acc[rb][h][0], acc[rb][h][1], acc[rb][h][2], acc[rb][h][3]};
+            if (vec) {
+                quad_transpose(v, qi);
+                const int64_t n = 32 * c + 16 * h + (lane & 12);
+                const int64_t r = m0 + 16 * rb + 4 * g + qi;
+                if (r >= M || n >= N) continue;
+                if (splits > 1)
+                    *reinterpret_cast<float4*>(partial + (z * M + r) * ncolP + (n - tile0 * kPkCols)) =
+                        make_float4(v[0], v[1], v[2], v[3]);
+                else if (y_bf16)
+                    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(Y) + r * N + n) =
+                        make_uint2((uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16),
+                                   (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16));
+                else
+                    *reinterpret_cast<float4*>(static_cast<float*>(Y) + r * N + n) = make_float4(v[0], v[1], v[2], v[3]);
+                continue;
+            }
+            const int64_t n = 32 * c + 16 * h + (lane & 15);
             if (n >= N) continue;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int64_t r = m0 + 16 * rb + 4 * (lane >> 4) + j;
+                const int64_t r = m0 + 16 * rb + 4 * g + j;
                 if (r >= M) continue;
-                const float v = acc[rb][h][j];
                 if (splits > 1)
-                    partial[(z * M + r) * ncolP + (n - tile0 * kPkCols)] = v;
+                    partial[(z * M + r) * ncolP + (n - tile0 * kPkCols)] = v[j];
                 else if (y_bf16)
-                    static_cast<uint16_t*>(Y)[r * N + n] = f32_to_bf16(v);
+                    static_cast<uint16_t*>(Y)[r * N + n] = f32_to_bf16(v[j]);
                 else
-                    static_cast<float*>(Y)[r * N + n] = v;
+                    static_cast<float*>(Y)[r * N + n] = v[j];
             }
         }
 }
