@@ -484,7 +484,7 @@ struct DmaCfg {
     static constexpr int XROWS = 1024 / (BK * 2), WROWS = 1024 / (BN * 2);  // rows per load
     static constexpr size_t LDS = (size_t)S * (XBYTES + WBYTES);
     static_assert(BK == 32 || BK == 64, "X swizzle covers 4 or 8 groups per row");
-    static_assert(BN == 64 || BN == 128 || BN == 256 || BN == 512, "whole W rows per load");
+    static_assert(BN == 128 || BN == 256 || BN == 512, "whole W rows per load; W swizzle over 16 groups");
     static_assert(XBYTES % 1024 == 0, "whole X rows per load");
     static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % NWM == 0 && BN % NWN == 0, "wave tile");
     static_assert(S >= 2 && (S - 2) * LMIN < 64, "ring depth / vmcnt range");
@@ -493,11 +493,18 @@ struct DmaCfg {
 
 // Physical 16-byte group of logical group g in X row r (BK = 32: 4 groups of
 // 64-byte rows; BK = 64: 8 groups of 128-byte rows), and in W row kr.
+//
+// LDS has 64 banks of 4 bytes.  A 16-lane pass of a 16-byte X read covers 16
+// rows of one logical group: the XOR spreads them over all 16 slots of 256
+// bytes.  A 32-lane pass of a transposed W read covers rows kr .. kr + 3 and
+// 4 logical groups 4q .. 4q + 3 (two lanes per group): W rows are a multiple
+// of 256 bytes (BN >= 128), so every row starts on bank 0, and XOR-ing the
+// group with 4 (kr & 3) gives each row its own 64 bytes of the 256.
 template <int XG>
 __device__ __forceinline__ int x_group(int g, int r) {
     return XG == 4 ? (g ^ ((r >> 2) & 3)) : (g ^ ((r >> 1) & 7));
 }
-__device__ __forceinline__ int w_group_tr(int g, int kr) { return g ^ (2 * (kr & 3)); }
+__device__ __forceinline__ int w_group_tr(int g, int kr) { return g ^ (4 * (kr & 3)); }
 
 // The LDS ring of S stage slots.  The loads that fill it are opaque to the
 // compiler (inline assembly with a memory clobber), so it neither waits for
